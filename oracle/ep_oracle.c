@@ -1,0 +1,340 @@
+/*
+ * ep_oracle.c -- plain, slow, single-threaded CPU oracle for MoE token
+ * dispatch and combine.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this file's library.  The product
+ * path (the HIP library and its Python binding) never calls it, and this file
+ * shares no code, header, table or constant generator with that path.
+ *
+ * What is computed and where it comes from.
+ *   DeepEP is the expert-parallel all-to-all library for Mixture-of-Experts
+ *   models: "dispatch" sends each token to the experts that its router picked
+ *   and "combine" brings the expert outputs back to the token
+ *   ("DeepSeek releases DeepEP, an efficient communication library for MoE
+ *   models", section "DeepEP: Optimizing MoE Communication"; the same two
+ *   operations are named in the introduction of "Deepseek Ai Deepep: A library
+ *   for an open-open EP for example training").  Dispatch may carry FP8
+ *   payloads (the feature list of "DeepSeek Open Source Weekly Review - 2"
+ *   names FP8 for dispatch).
+ *
+ *   The pages give neither the bookkeeping (layout) that an all-to-all needs,
+ *   nor the receive-buffer order, nor the FP8 scale rule, nor the combine
+ *   arithmetic.  This oracle takes the plainest reading of each, as listed
+ *   in the repository's design notes:
+ *     - expert e lives in partition floor(e / (E/P))              (contiguous)
+ *     - one receive row per valid (token, slot) pair, rows grouped by expert
+ *       in ascending expert order, so every partition is one contiguous run
+ *     - inside one expert's rows the order is by source token, then by slot
+ *     - topk_idx == -1 is a masked slot; any other value outside [0, E) is an
+ *       invalid slot: it is masked too and counted as an error
+ *     - per-partition token counts count distinct tokens
+ *     - FP8 is OCP E4M3 (bias 7, max finite 448, one NaN pattern per sign),
+ *       round to nearest even, saturating, sign kept; one fp32 scale per
+ *       token and 128 consecutive channels: a = max|x|, a_c = max(a, 1e-4f),
+ *       q = E4M3(x * (448 / a_c)), s = a_c / 448
+ *     - combine: out = bf16_rne( fma chain over slots k = 0..K-1 of
+ *       w[t][k] * y[dst[t][k]] in fp32, starting from +0, skipping masked
+ *       slots )
+ *
+ * Build: gcc -O2 -std=c99 -ffp-contract=off -fno-fast-math -fPIC -shared.
+ * Contraction is off so that every float product and sum below rounds on its
+ * own, exactly as written; fmaf() is the only fused operation.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Scalar formats                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* bf16 -> fp32 is exact: a bf16 value is the top half of an fp32 word. */
+static float bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/*
+ * fp32 -> bf16, round to nearest, ties to even.
+ * Written from the definition: take the two bf16 values that bracket |f|
+ * (truncation and the next one up), measure both distances exactly in double,
+ * keep the nearer, and on a tie keep the one whose last mantissa bit is 0.
+ * The next value up from the largest finite bf16 is 2^128, which rounds to
+ * infinity, as IEEE round-to-nearest prescribes.
+ */
+uint16_t oracle_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    if (isnan(f))
+        return (uint16_t)(sign | 0x7FC0u);
+    if (isinf(f))
+        return (uint16_t)(sign | 0x7F80u);
+
+    uint16_t lo = (uint16_t)((u >> 16) & 0x7FFFu); /* |f| truncated */
+    uint16_t hi = (uint16_t)(lo + 1u);             /* next bf16 magnitude up */
+    double a = fabs((double)f);
+    double vlo = (double)bf16_to_f32(lo);
+    double vhi = (hi == 0x7F80u) ? ldexp(1.0, 128) : (double)bf16_to_f32(hi);
+    double dlo = a - vlo, dhi = vhi - a;
+    uint16_t mag;
+    if (dlo < dhi)
+        mag = lo;
+    else if (dhi < dlo)
+        mag = hi;
+    else
+        mag = (lo & 1u) ? hi : lo;
+    return (uint16_t)(sign | mag);
+}
+
+/*
+ * fp32 -> OCP E4M3 ("e4m3fn"), round to nearest even, saturating.
+ * Format: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits.  Normal
+ * codes are (1 + m/8) * 2^(e-7) for e = 1..15; code S.1111.111 is NaN, so the
+ * largest finite value is 1.75 * 2^8 = 448 (0x7E).  Subnormal codes
+ * (e = 0) are (m/8) * 2^-6.
+ *
+ * Every finite E4M3 value is an integer multiple of the quantum of its
+ * binade: 2^(E-3) for |v| in [2^E, 2^(E+1)), E >= -6, and the subnormals
+ * share the quantum 2^-9 of binade -6.  So the encoder finds the binade,
+ * divides by the quantum (exact: a power of two) and rounds to the nearest
+ * integer with nearbyint() under the default ties-to-even mode.  A result of
+ * 16 quanta carries into the next binade.  Magnitudes at or above 448
+ * saturate to 448; the sign bit is always kept, so a negative value that
+ * rounds to zero gives 0x80.
+ */
+uint8_t oracle_e4m3(float v)
+{
+    uint8_t sign = signbit(v) ? 0x80u : 0x00u;
+    if (isnan(v))
+        return (uint8_t)(sign | 0x7Fu);
+    double a = fabs((double)v);
+    if (a >= 448.0)
+        return (uint8_t)(sign | 0x7Eu);
+    if (a == 0.0)
+        return sign;
+
+    int ex;
+    (void)frexp(a, &ex); /* a = f * 2^ex with f in [0.5, 1) */
+    int E = ex - 1;      /* a in [2^E, 2^(E+1)) */
+    if (E < -6)
+        E = -6;          /* subnormal range: quantum of binade -6 */
+    double q = nearbyint(a / ldexp(1.0, E - 3));
+    if (q >= 16.0) {     /* rounded up into the next binade */
+        E += 1;
+        q = 8.0;
+    }
+    int code;
+    if (E == -6 && q < 8.0)
+        code = (int)q;                          /* subnormal */
+    else
+        code = ((E + 7) << 3) | ((int)q - 8);  /* normal */
+    if (code > 0x7E)
+        code = 0x7E;     /* unreachable for a < 448; kept as the saturation rule */
+    return (uint8_t)(sign | (uint8_t)code);
+}
+
+/* Element-wise array forms, for the tests' sweeps. */
+void oracle_bf16_rne_array(const float *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_bf16_rne(in[i]);
+}
+
+void oracle_e4m3_array(const float *in, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_e4m3(in[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Layout: per-expert / per-partition counts and offsets                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The bookkeeping every all-to-all dispatch needs before it can move data:
+ * how many rows go to each expert and to each destination partition, and
+ * where each run starts ("DeepSeek releases DeepEP ...", section "DeepEP:
+ * Optimizing MoE Communication": efficient all-to-all between the GPUs that
+ * host the experts).
+ *
+ *   idx          [T][K] int64, row-major
+ *   cnt_e        [E]    rows routed to expert e (valid slots only)
+ *   cnt_p        [P]    distinct tokens with at least one valid slot in p
+ *   in_part      [T][P] 1 if token t has a valid slot in partition p, else 0
+ *   off_e        [E+1]  exclusive prefix sum of cnt_e; off_e[E] = N
+ *   off_p        [P+1]  off_p[p] = off_e[p * (E/P)]
+ * Returns the number of invalid slots (outside [0, E) and not -1).
+ */
+int64_t oracle_layout(const int64_t *idx, int32_t T, int32_t K, int32_t E, int32_t P,
+                      int32_t *cnt_e, int32_t *cnt_p, uint8_t *in_part,
+                      int32_t *off_e, int32_t *off_p)
+{
+    int32_t Ep = E / P;
+    int64_t nerr = 0;
+    for (int32_t e = 0; e < E; ++e)
+        cnt_e[e] = 0;
+    for (int32_t p = 0; p < P; ++p)
+        cnt_p[p] = 0;
+    for (int64_t i = 0; i < (int64_t)T * P; ++i)
+        in_part[i] = 0;
+
+    for (int32_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int64_t v = idx[(int64_t)t * K + k];
+            if (v >= 0 && v < E) {
+                cnt_e[v] += 1;
+                in_part[(int64_t)t * P + v / Ep] = 1;
+            } else if (v != -1) {
+                nerr += 1;
+            }
+        }
+    }
+    for (int32_t t = 0; t < T; ++t)
+        for (int32_t p = 0; p < P; ++p)
+            cnt_p[p] += in_part[(int64_t)t * P + p];
+
+    off_e[0] = 0;
+    for (int32_t e = 0; e < E; ++e)
+        off_e[e + 1] = off_e[e] + cnt_e[e];
+    for (int32_t p = 0; p <= P; ++p)
+        off_p[p] = off_e[p * Ep];
+    return nerr;
+}
+
+/*
+ * Receive-row assignment.  Valid slots are visited in (token, slot) order and
+ * each takes the next free row of its expert's run, so inside an expert the
+ * rows are ordered by source token, then slot.
+ *   dst [T][K]  receive row of slot (t,k), or -1 for a masked/invalid slot
+ *   src [T*K]   source token of receive row r, or -1 for r >= N
+ */
+void oracle_permutation(const int64_t *idx, int32_t T, int32_t K, int32_t E,
+                        const int32_t *off_e, int32_t *dst, int32_t *src)
+{
+    int32_t *next = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    int32_t N = off_e[E];
+    for (int32_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int64_t v = idx[(int64_t)t * K + k];
+            if (v >= 0 && v < E) {
+                int32_t r = off_e[v] + next[v];
+                next[v] += 1;
+                dst[(int64_t)t * K + k] = r;
+                src[r] = t;
+            } else {
+                dst[(int64_t)t * K + k] = -1;
+            }
+        }
+    }
+    for (int64_t r = N; r < (int64_t)T * K; ++r)
+        src[r] = -1;
+    free(next);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dispatch                                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* bf16 dispatch: receive row r is a bitwise copy of token src[r], r < N. */
+void oracle_dispatch_bf16(const uint16_t *x, int32_t T, int32_t H,
+                          const int32_t *src, int32_t N, uint16_t *recv_x)
+{
+    (void)T;
+    for (int64_t r = 0; r < N; ++r) {
+        int64_t t = src[r];
+        for (int64_t h = 0; h < H; ++h)
+            recv_x[r * H + h] = x[t * H + h];
+    }
+}
+
+/*
+ * Per-token FP8 quantisation with one scale per 128 consecutive channels
+ * (FP8 for dispatch is in the feature list of "DeepSeek Open Source Weekly
+ * Review - 2"; FP8 support is also listed in "DeepSeek releases DeepEP ...",
+ * section "DeepEP: Optimizing MoE Communication").  For token t and group
+ * g (channels 128g .. 128g+127):
+ *   a    = max |x|                (exact in fp32)
+ *   a_c  = max(a, 1e-4f)
+ *   inv  = 448.0f / a_c           (one correctly rounded fp32 division)
+ *   s    = a_c / 448.0f           (one correctly rounded fp32 division)
+ *   q[h] = E4M3(x[h] * inv)       (one rounded fp32 product, then encode)
+ *   q [T][H] bytes, s [T][H/128] fp32.  H must be a multiple of 128.
+ */
+void oracle_quantize(const uint16_t *x, int32_t T, int32_t H, uint8_t *q, float *s)
+{
+    int32_t G = H / 128;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t g = 0; g < G; ++g) {
+            float a = 0.0f;
+            for (int32_t j = 0; j < 128; ++j) {
+                float v = fabsf(bf16_to_f32(x[t * H + 128 * g + j]));
+                if (v > a)
+                    a = v;
+            }
+            float ac = (a > 1e-4f) ? a : 1e-4f;
+            float inv = 448.0f / ac;
+            s[t * G + g] = ac / 448.0f;
+            for (int32_t j = 0; j < 128; ++j) {
+                float prod = bf16_to_f32(x[t * H + 128 * g + j]) * inv;
+                q[t * H + 128 * g + j] = oracle_e4m3(prod);
+            }
+        }
+    }
+}
+
+/* FP8 dispatch: receive row r (r < N) gets token src[r]'s codes and scales. */
+void oracle_dispatch_fp8(const uint16_t *x, int32_t T, int32_t H,
+                         const int32_t *src, int32_t N,
+                         uint8_t *recv_x, float *recv_scales)
+{
+    int32_t G = H / 128;
+    uint8_t *q = (uint8_t *)malloc((size_t)T * (size_t)H + 1);
+    float *s = (float *)malloc(((size_t)T * (size_t)G + 1) * sizeof(float));
+    oracle_quantize(x, T, H, q, s);
+    for (int64_t r = 0; r < N; ++r) {
+        int64_t t = src[r];
+        for (int64_t h = 0; h < H; ++h)
+            recv_x[r * H + h] = q[t * H + h];
+        for (int32_t g = 0; g < G; ++g)
+            recv_scales[r * G + g] = s[t * G + g];
+    }
+    free(q);
+    free(s);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Combine                                                                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Combine: bring the expert outputs of a token back and reduce them with the
+ * token's gate weights ("DeepSeek releases DeepEP ...", section "DeepEP:
+ * Optimizing MoE Communication").  For every token t and channel h:
+ *   acc = +0.0f
+ *   for k = 0 .. K-1 with dst[t][k] >= 0:  acc = fmaf(w[t][k], y[dst[t][k]][h], acc)
+ *   out[t][h] = bf16_rne(acc)
+ *   y [R][H] bf16 (R >= max dst + 1), w [T][K] fp32, out [T][H] bf16.
+ */
+void oracle_combine(const uint16_t *y, const int32_t *dst, const float *w,
+                    int32_t T, int32_t K, int32_t H, uint16_t *out)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int32_t k = 0; k < K; ++k) {
+                int64_t r = dst[t * K + k];
+                if (r < 0)
+                    continue;
+                acc = fmaf(w[t * K + k], bf16_to_f32(y[r * H + h]), acc);
+            }
+            out[t * H + h] = oracle_bf16_rne(acc);
+        }
+    }
+}

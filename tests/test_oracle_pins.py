@@ -1,0 +1,388 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+* hand-worked fixtures under tests/golden/ (format definitions, a worked layout
+  and combine example);
+* exhaustive search over the 256 E4M3 codes for every bf16 pattern and a dense
+  fp32 sweep, plus torch's CPU float8_e4m3fn cast in range;
+* torch's CPU bf16 cast for the bf16 rounding;
+* library routines (stable argsort, bincount, cumsum) and pairwise brute force
+  for the layout and permutation, exhaustively over every routing tensor with
+  T*K <= 6 and ids in {-1, 0..3};
+* invariants of the quantiser and exact rational arithmetic / closed forms for
+  combine.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import bruteforce as bf
+from combine_ep_get_dispatch_amd import workloads as wl
+
+
+def _read_kv(path):
+    out = {}
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        k, *v = line.split()
+        out[k] = v
+    return out
+
+
+def _read_points(path):
+    rows = []
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        parts = line.split()
+        rows.append((float(parts[0]), int(parts[1], 16)))
+    return rows
+
+
+# ---------------------------------------------------------------------------
+# scalar formats
+# ---------------------------------------------------------------------------
+
+def test_e4m3_golden_points(golden_dir):
+    pts = _read_points(os.path.join(golden_dir, "e4m3_points.txt"))
+    v = np.array([p[0] for p in pts], np.float32)
+    want = np.array([p[1] for p in pts], np.uint8)
+    np.testing.assert_array_equal(oracle.e4m3(v), want)
+    np.testing.assert_array_equal(bf.e4m3_nearest(v), want)
+
+
+def test_e4m3_all_bf16_patterns_times_scales():
+    """Every finite bf16 value, times a set of scales, encoded by the oracle
+    equals the exhaustive nearest-code search."""
+    bits = np.arange(65536, dtype=np.uint32)
+    vals = ((bits << 16).view(np.float32))
+    vals = vals[np.isfinite(vals)]
+    for mult in [1.0, 0.5, 3.0, 448.0 / 3.1, 1.0 / 7.0, 2.0 ** -8, 1.37e-3]:
+        with np.errstate(over="ignore"):
+            v = (vals * np.float32(mult)).astype(np.float32)
+        v = v[np.isfinite(v)]
+        np.testing.assert_array_equal(oracle.e4m3(v), bf.e4m3_nearest(v), err_msg=str(mult))
+
+
+def test_e4m3_dense_sweep_and_torch():
+    v = np.linspace(-464.0, 464.0, 400_001, dtype=np.float64).astype(np.float32)
+    # add every midpoint between neighbouring codes and one fp32 step either side
+    mags = bf.e4m3_decode_table()[:0x7F]
+    mids = ((mags[1:] + mags[:-1]) / 2).astype(np.float32)
+    near = np.concatenate([mids, np.nextafter(mids, np.float32(0)),
+                           np.nextafter(mids, np.float32(1000))])
+    v = np.concatenate([v, near, -near])
+    got = oracle.e4m3(v)
+    np.testing.assert_array_equal(got, bf.e4m3_nearest(v))
+    # torch's cast is round-to-nearest-even in range (it gives NaN beyond 464)
+    inr = np.abs(v) <= 448
+    t = torch.from_numpy(v[inr]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(got[inr], t)
+
+
+def test_bf16_golden_points(golden_dir):
+    pts = _read_points(os.path.join(golden_dir, "bf16_points.txt"))
+    v = np.array([p[0] for p in pts], np.float32)
+    want = np.array([p[1] for p in pts], np.uint16)
+    np.testing.assert_array_equal(oracle.bf16_rne(v), want)
+
+
+def test_bf16_rne_against_torch():
+    rng = np.random.default_rng(7)
+    u = rng.integers(0, 2 ** 32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
+    v = u.view(np.float32)
+    v = v[np.isfinite(v)]
+    # exact ties: a bf16 value plus half its step
+    b = rng.integers(0, 0x7F7F, size=100_000).astype(np.uint32) << 16
+    ties = (b | 0x8000).view(np.float32)
+    v = np.concatenate([v, ties, -ties, np.float32([0.0, -0.0, 1e-45, -1e-45])])
+    want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.bf16_rne(v), want)
+
+
+# ---------------------------------------------------------------------------
+# layout and permutation
+# ---------------------------------------------------------------------------
+
+def _check_against_bruteforce(idx, E, P):
+    got = oracle.layout(idx, E, P)
+    want = bf.layout(idx, E, P)
+    for k in want:
+        np.testing.assert_array_equal(np.asarray(got[k]), np.asarray(want[k]), err_msg=k)
+    dst, src = oracle.permutation(idx, E, got["expert_offsets"])
+    bdst, bsrc = bf.permutation(idx, E)
+    np.testing.assert_array_equal(dst, bdst)
+    np.testing.assert_array_equal(src, bsrc)
+    return got, dst, src
+
+
+def test_layout_hand_worked(golden_dir):
+    g = _read_kv(os.path.join(golden_dir, "layout_hand_worked.txt"))
+    T, K, E, P = (int(g[k][0]) for k in "TKEP")
+    idx = np.array(g["topk_idx"], np.int64).reshape(T, K)
+    lay = oracle.layout(idx, E, P)
+    for key in ["num_tokens_per_expert", "expert_offsets", "num_tokens_per_partition",
+                "partition_offsets"]:
+        np.testing.assert_array_equal(lay[key], np.array(g[key], np.int32), err_msg=key)
+    np.testing.assert_array_equal(lay["is_token_in_partition"].reshape(-1),
+                                  np.array(g["is_token_in_partition"], np.uint8))
+    dst, src = oracle.permutation(idx, E, lay["expert_offsets"])
+    np.testing.assert_array_equal(dst.reshape(-1), np.array(g["dst_row"], np.int32))
+    np.testing.assert_array_equal(src, np.array(g["recv_src_token"], np.int32))
+
+
+def test_combine_hand_worked(golden_dir):
+    g = _read_kv(os.path.join(golden_dir, "layout_hand_worked.txt"))
+    T, K, H = int(g["T"][0]), int(g["K"][0]), int(g["H"][0])
+    dst = np.array(g["dst_row"], np.int32).reshape(T, K)
+    w = np.array(g["topk_weights"], np.float32).reshape(T, K)
+    y = np.array([int(b, 16) for b in g["y_bits_hex"]], np.uint16).reshape(-1, H)
+    want = np.array([int(b, 16) for b in g["out_bits_hex"]], np.uint16).reshape(T, H)
+    np.testing.assert_array_equal(oracle.combine(y, dst, w), want)
+
+
+@pytest.mark.parametrize("T,K", [(1, 6), (2, 3), (3, 2), (6, 1), (2, 2), (1, 1)])
+def test_layout_exhaustive_small(T, K):
+    """Every routing tensor of this shape with ids in {-1, 0, 1, 2, 3} (masked
+    slots and repeated experts included), E = 4, P in {1, 2, 4}."""
+    E = 4
+    n = T * K
+    grid = np.array(np.meshgrid(*[np.arange(-1, E)] * n, indexing="ij")).reshape(n, -1).T
+    batch = grid.reshape(-1, T, K).astype(np.int64)
+    dst_ref = None
+    for P in (1, 2, 4):
+        cnt_e, in_part, off_e, dst_b, nerr = bf.layout_batch(batch, E, P)
+        for i in range(batch.shape[0]):
+            got = oracle.layout(batch[i], E, P)
+            assert np.array_equal(got["num_tokens_per_expert"], cnt_e[i])
+            assert np.array_equal(got["is_token_in_partition"], in_part[i])
+            assert np.array_equal(got["expert_offsets"], off_e[i])
+            assert np.array_equal(got["num_tokens_per_partition"], in_part[i].sum(axis=0))
+            assert np.array_equal(got["partition_offsets"], off_e[i][np.arange(P + 1) * (E // P)])
+            assert got["num_invalid"] == 0 == nerr[i]
+            if P == 1:
+                dst, src = oracle.permutation(batch[i], E, got["expert_offsets"])
+                assert np.array_equal(dst, dst_b[i]), (batch[i], dst, dst_b[i])
+                N = off_e[i][E]
+                # src is the inverse of dst on [0, N), and -1 beyond
+                inv = np.full(T * K, -1, np.int32)
+                for t in range(T):
+                    for k in range(K):
+                        if dst[t, k] >= 0:
+                            inv[dst[t, k]] = t
+                assert np.array_equal(src, inv) and (src[N:] == -1).all()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_layout_random_against_library_routines(seed):
+    rng = np.random.default_rng(seed)
+    E = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+    P = int(rng.choice([d for d in (1, 2, 4, 8, 16, 32) if E % d == 0]))
+    K = int(rng.integers(1, min(E, 8) + 1))
+    T = int(rng.integers(0, 300))
+    c = wl.random_case(T, 8, E, P, K, seed, masked_frac=0.1 * (seed % 3),
+                       allow_dup=bool(seed % 2), skew=float(seed % 4), with_y=False)
+    got, dst, src = _check_against_bruteforce(c.topk_idx, E, P)
+    N = got["expert_offsets"][E]
+    # invariants: bijection of valid slots onto [0, N), segment membership, order
+    valid = dst >= 0
+    assert sorted(dst[valid].tolist()) == list(range(N))
+    assert np.all(src[dst[valid]] == np.nonzero(valid)[0])
+    for e in range(E):
+        seg = src[got["expert_offsets"][e]:got["expert_offsets"][e + 1]]
+        assert np.all(np.diff(seg) >= 0)
+    Tn = T
+    assert Tn <= got["num_tokens_per_partition"].sum() + (~valid.any(axis=1)).sum() or T == 0
+    assert got["num_tokens_per_partition"].sum() <= T * min(K, P)
+
+
+def test_layout_invalid_ids_are_masked_and_counted():
+    c = wl.random_case(200, 8, 32, 8, 4, 5, masked_frac=0.1, invalid_frac=0.1, with_y=False)
+    got, dst, src = _check_against_bruteforce(c.topk_idx, 32, 8)
+    bad = (c.topk_idx != -1) & ((c.topk_idx < 0) | (c.topk_idx >= 32))
+    assert got["num_invalid"] == int(bad.sum()) > 0
+    assert np.all(dst[bad] == -1) and np.all(dst[c.topk_idx == -1] == -1)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skewed", "coarse"])
+def test_layout_of_each_configuration(name):
+    cfg = wl.CONFIGS[name]
+    idx, w, meta = wl.route(cfg)
+    assert idx.shape == (cfg["T"], cfg["K"])
+    got, dst, src = _check_against_bruteforce(idx, cfg["E"], cfg["P"])
+    assert got["expert_offsets"][-1] == cfg["T"] * cfg["K"]          # every slot valid
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-6)
+    if name == "prefill":
+        assert meta["groups_per_token_max"] <= cfg["topk_groups"]
+    if name == "skewed":
+        assert meta["max_over_mean_load"] >= 10.0
+
+
+# ---------------------------------------------------------------------------
+# FP8 quantiser
+# ---------------------------------------------------------------------------
+
+def _quant_numpy(x_bits):
+    """The quantiser's steps in numpy fp32 arithmetic, with the exhaustive
+    nearest-code encoder (numpy's fp32 division and product round correctly)."""
+    x = bf.bf16_bits_to_f32(x_bits)
+    T, H = x.shape
+    g = x.reshape(T, H // 128, 128)
+    a = np.abs(g).max(axis=2)
+    ac = np.maximum(a, np.float32(1e-4)).astype(np.float32)
+    inv = (np.float32(448.0) / ac).astype(np.float32)
+    s = (ac / np.float32(448.0)).astype(np.float32)
+    prod = (g * inv[:, :, None]).astype(np.float32)
+    q = bf.e4m3_nearest(prod.reshape(-1)).reshape(T, H)
+    return q, s
+
+
+def test_quantize_matches_numpy_steps_and_invariants():
+    rng = np.random.default_rng(3)
+    T, H = 48, 1024
+    xf = rng.standard_normal((T, H), dtype=np.float32)
+    xf[0, :128] = 0.0                                  # all-zero group
+    xf[1, 128:256] = -0.0                              # all negative zero
+    xf[2, 256:384] *= 1e-6                             # amax below the 1e-4 floor
+    xf[3, :] *= 1e4
+    xf[4, 512:640] = 3.0                               # constant group
+    xb = wl.bf16_bits_from_f32(xf)
+    q, s = oracle.quantize(xb)
+    nq, ns = _quant_numpy(xb)
+    np.testing.assert_array_equal(q, nq)
+    np.testing.assert_array_equal(s.view(np.uint32), ns.view(np.uint32))
+
+    x = bf.bf16_bits_to_f32(xb).reshape(T, H // 128, 128)
+    qg = q.reshape(T, H // 128, 128)
+    amax = np.abs(x).max(axis=2)
+    big = amax >= 1e-4
+    # (i) the largest-magnitude element of a group encodes to +-448
+    for t, g in zip(*np.nonzero(big)):
+        j = np.argmax(np.abs(x[t, g]))
+        assert qg[t, g, j] & 0x7F == 0x7E
+    # (ii) reconstruction error bound: half a step of E4M3 relative to the value,
+    # or half a subnormal step, times the scale, plus fp32 slack
+    dec = bf.e4m3_decode_table()[qg].astype(np.float64) * s[:, :, None]
+    err = np.abs(dec - x)
+    bound = 2.0 ** -4 * np.abs(x) + 2.0 ** -10 * s[:, :, None] + 4 * 2.0 ** -24 * np.abs(x)
+    assert np.all(err <= bound)
+    # (iii) zero groups: codes are signed zeros and the scale is 1e-4/448
+    zs = np.float32(np.float32(1e-4) / np.float32(448.0))
+    assert s[0, 0] == zs and s[1, 1] == zs
+    assert np.all(qg[0, 0] == 0x00) and np.all(qg[1, 1] == 0x80)
+
+
+def test_fp8_dispatch_rows_are_quantised_tokens():
+    c = wl.random_case(70, 384, 16, 4, 3, 11, masked_frac=0.1)
+    res = oracle.run(c.topk_idx, c.x_bits, 16, 4, fp8=True)
+    q, s = oracle.quantize(c.x_bits)
+    N = res["expert_offsets"][16]
+    src = res["recv_src_token"][:N]
+    np.testing.assert_array_equal(res["recv_x"][:N], q[src])
+    np.testing.assert_array_equal(res["recv_scales"][:N], s[src])
+
+
+def test_bf16_dispatch_rows_are_bitwise_copies():
+    c = wl.random_case(90, 264, 12, 3, 4, 12, masked_frac=0.05, allow_dup=True)
+    res = oracle.run(c.topk_idx, c.x_bits, 12, 3, fp8=False)
+    T, K = c.topk_idx.shape
+    for t in range(T):
+        for k in range(K):
+            r = res["dst_row"][t, k]
+            if r >= 0:
+                assert np.array_equal(res["recv_x"][r], c.x_bits[t])
+
+
+# ---------------------------------------------------------------------------
+# combine
+# ---------------------------------------------------------------------------
+
+def test_combine_exact_rational_small():
+    """Exact rational evaluation of each fused step on small random cases,
+    including masked slots and weights of both signs."""
+    rng = np.random.default_rng(5)
+    for trial in range(6):
+        T, K, H = 5, int(rng.integers(1, 5)), 7
+        R = T * K
+        dst = rng.permutation(R).reshape(T, K).astype(np.int32)
+        dst[rng.random((T, K)) < 0.2] = -1
+        w = (rng.standard_normal((T, K)) * 3).astype(np.float32)
+        y = wl.bf16_bits_from_f32(rng.standard_normal((R, H), dtype=np.float32) * 10)
+        np.testing.assert_array_equal(oracle.combine(y, dst, w), bf.combine_exact(y, dst, w))
+
+
+def test_combine_closed_forms():
+    rng = np.random.default_rng(9)
+    T, K, H = 40, 4, 96
+    R = T * K
+    dst = rng.permutation(R).reshape(T, K).astype(np.int32)
+    # powers of two times small integers: every step is exact
+    w = rng.choice(np.float32([0.5, 1.0, 2.0, -1.0]), size=(T, K)).astype(np.float32)
+    yi = rng.integers(-4, 5, size=(R, H)).astype(np.float32)
+    y = wl.bf16_bits_from_f32(yi)
+    want = (w[:, :, None] * yi[dst]).sum(axis=1)
+    got = bf.bf16_bits_to_f32(oracle.combine(y, dst, w))
+    np.testing.assert_array_equal(got, want.astype(np.float32))
+    # K = 1, w = 1: combine returns the rows themselves
+    d1 = rng.permutation(R)[:T].reshape(T, 1).astype(np.int32)
+    y2 = wl.bf16_bits_from_f32(rng.standard_normal((R, H), dtype=np.float32))
+    out = oracle.combine(y2, d1, np.ones((T, 1), np.float32))
+    np.testing.assert_array_equal(out, y2[d1[:, 0]])
+
+
+def test_combine_identity_expert_and_fp64_bound():
+    """y = the bf16 dispatch output (identity experts): out ~ (sum_k w) * x;
+    and everywhere within the fp32 FMA-chain bound of the exact float64 sum."""
+    c = wl.random_case(64, 512, 16, 4, 4, 21)
+    w = c.topk_weights / c.topk_weights.sum(axis=1, keepdims=True)
+    res = oracle.run(c.topk_idx, c.x_bits, 16, 4, fp8=False)
+    out = bf.bf16_bits_to_f32(oracle.combine(res["recv_x"], res["dst_row"], w))
+    x = bf.bf16_bits_to_f32(c.x_bits).astype(np.float64)
+    exact = w.astype(np.float64).sum(axis=1, keepdims=True) * x
+    K = 4
+    bound = 2.0 ** -8 * np.abs(exact) + K * 2.0 ** -24 * np.abs(x) * 1.01 + 1e-38
+    assert np.all(np.abs(out - exact) <= bound)
+    # general weights: float64 sum of the products
+    y = bf.bf16_bits_to_f32(c.y_bits).astype(np.float64)
+    dst = res["dst_row"]
+    prod = c.topk_weights.astype(np.float64)[:, :, None] * y[dst]
+    exact = prod.sum(axis=1)
+    out = bf.bf16_bits_to_f32(oracle.combine(c.y_bits, dst, c.topk_weights))
+    bound = 2.0 ** -8 * np.abs(exact) + (K + 1) * 2.0 ** -24 * np.abs(prod).sum(axis=1)
+    assert np.all(np.abs(out - exact) <= bound)
+
+
+def test_combine_rounding_sensitive_cases():
+    """Cases built to land next to a bf16 rounding boundary, where the fused
+    multiply-add, the slot order and the single final rounding decide the last
+    bit: acc = 1 from slot 0, then a slot-1 product of about 2^-8 + 2^-24 with
+    random low bits.  The exact rational evaluation of the fused chain is the
+    reference; the test also checks that an unfused or reversed evaluation
+    would differ on a good share of these cases, so they do discriminate."""
+    from fractions import Fraction
+    rng = np.random.default_rng(17)
+    n = 256
+    y2 = wl.bf16_bits_from_f32(rng.uniform(2.0 ** -9, 2.0 ** -7, n).astype(np.float32))
+    y2f = bf.bf16_bits_to_f32(y2).astype(np.float64)
+    target = 2.0 ** -8 + 2.0 ** -24 + rng.uniform(-1, 1, n) * 2.0 ** -32
+    w2 = (target / y2f).astype(np.float32)
+    T, K, H = n, 2, 1
+    y = np.empty((2 * n, 1), np.uint16)
+    y[0::2, 0] = 0x3F80                      # 1.0
+    y[1::2, 0] = y2
+    dst = np.stack([np.arange(0, 2 * n, 2), np.arange(1, 2 * n, 2)], axis=1).astype(np.int32)
+    w = np.stack([np.ones(n, np.float32), w2], axis=1)
+    want = bf.combine_exact(y, dst, w)
+    np.testing.assert_array_equal(oracle.combine(y, dst, w), want)
+    # discrimination: evaluate the unfused chain exactly and count differences
+    differ = 0
+    for i in range(n):
+        p = bf.f32_round(Fraction(float(w2[i])) * Fraction(float(y2f[i])))
+        unfused = bf.bf16_round_bits(Fraction(bf.f32_round(Fraction(1) + Fraction(p))))
+        differ += int(unfused != want[i, 0])
+    assert differ >= n // 8, differ
