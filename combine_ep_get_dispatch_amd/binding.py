@@ -1,0 +1,256 @@
+"""Thin ctypes binding of libep_mi355x.so (include/ep.h) for torch tensors.
+
+Argument marshalling only: every step of dispatch and combine runs in the HIP
+kernels behind the C ABI; torch provides device memory and the current
+stream.  The functions allocate their outputs with ``torch.empty`` unless
+``out``-style arguments are passed (the benchmark passes them so that nothing
+is allocated in its timed loop).  If the library is not built the first call
+raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libep_mi355x.so")
+
+EP_OK = 0
+EP_DTYPE_BF16 = 0
+EP_DTYPE_FP8_E4M3 = 1
+MAX_EXPERTS = 1024
+MAX_TOPK = 64
+
+
+class EpError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s" % (what, status_string(status)))
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+
+SIGNATURES = {
+    "ep_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "ep_get_dispatch_layout": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                              _vp, _vp, _sz, _vp]),
+    "ep_dispatch": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _i32, ctypes.c_int, _vp,
+                                   _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ep_combine": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "ep_get_device_error": (ctypes.c_int, [_vp, _sz, ctypes.POINTER(_i64), _vp]),
+    "ep_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "ep_convert_e4m3": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp]),
+    "ep_convert_bf16": (ctypes.c_int, [_vp, _vp, _i64, _vp]),
+    "ep_copy": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
+}
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libep_mi355x.so is not built: run `python -m combine_ep_get_dispatch_amd.build`"
+                " (or __graft_entry__.build()) first")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ep_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != EP_OK:
+        raise EpError(status, what)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, dtype, name: str, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+# ---------------------------------------------------------------------------
+# layout
+# ---------------------------------------------------------------------------
+
+def workspace_bytes(num_tokens: int, num_topk: int, num_experts: int, num_partitions: int) -> int:
+    n = lib().ep_workspace_bytes(num_tokens, num_topk, num_experts, num_partitions)
+    if n == 0:
+        raise ValueError("invalid shape T=%d K=%d E=%d P=%d" % (
+            num_tokens, num_topk, num_experts, num_partitions))
+    return int(n)
+
+
+def new_workspace(num_tokens, num_topk, num_experts, num_partitions, device="cuda"):
+    """A zero-filled workspace for this shape (the header must start at zero)."""
+    return torch.zeros(workspace_bytes(num_tokens, num_topk, num_experts, num_partitions),
+                       dtype=torch.uint8, device=device)
+
+
+@dataclass
+class Layout:
+    num_tokens_per_expert: torch.Tensor     # [E] int32
+    num_tokens_per_partition: torch.Tensor  # [P] int32
+    is_token_in_partition: torch.Tensor     # [T, P] uint8
+    expert_offsets: torch.Tensor            # [E+1] int32
+    partition_offsets: torch.Tensor         # [P+1] int32
+    workspace: torch.Tensor                 # uint8, consumed by dispatch
+
+
+def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_partitions: int,
+                        workspace: torch.Tensor | None = None,
+                        out: Layout | None = None) -> Layout:
+    """ep_get_dispatch_layout on ``topk_idx`` [T, K] int64."""
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [T, K]")
+    T, K = topk_idx.shape
+    _need(topk_idx, torch.int64, "topk_idx")
+    dev = topk_idx.device
+    E, P = int(num_experts), int(num_partitions)
+    if workspace is None:
+        workspace = new_workspace(T, K, E, P, dev)
+    _need(workspace, torch.uint8, "workspace")
+    if out is None:
+        out = Layout(torch.empty(E, dtype=torch.int32, device=dev),
+                     torch.empty(P, dtype=torch.int32, device=dev),
+                     torch.empty((T, P), dtype=torch.uint8, device=dev),
+                     torch.empty(E + 1, dtype=torch.int32, device=dev),
+                     torch.empty(P + 1, dtype=torch.int32, device=dev), workspace)
+    else:
+        out.workspace = workspace
+    _check(lib().ep_get_dispatch_layout(
+        _ptr(topk_idx), T, K, E, P, _ptr(out.num_tokens_per_expert),
+        _ptr(out.num_tokens_per_partition), _ptr(out.is_token_in_partition),
+        _ptr(out.expert_offsets), _ptr(out.partition_offsets), _ptr(workspace),
+        workspace.numel(), _stream(topk_idx)), "ep_get_dispatch_layout")
+    return out
+
+
+def get_device_error(workspace: torch.Tensor) -> int:
+    """Invalid topk_idx entries met by the last layout call (synchronises)."""
+    n = _i64(0)
+    _check(lib().ep_get_device_error(_ptr(workspace), workspace.numel(), ctypes.byref(n),
+                                     _stream(workspace)), "ep_get_device_error")
+    return int(n.value)
+
+
+# ---------------------------------------------------------------------------
+# dispatch / combine
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Dispatched:
+    recv_x: torch.Tensor                 # [T*K, H] bf16, or uint8 E4M3 codes
+    recv_scales: torch.Tensor | None     # [T*K, H/128] float32 (FP8 only)
+    recv_src_token: torch.Tensor         # [T*K] int32
+    dst_row: torch.Tensor                # [T, K] int32
+
+
+def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_partitions: int,
+             workspace: torch.Tensor, fp8: bool = False,
+             out: Dispatched | None = None) -> Dispatched:
+    """ep_dispatch: x [T, H] bf16 -> receive rows grouped by expert."""
+    if x.dim() != 2 or topk_idx.dim() != 2:
+        raise ValueError("x must be [T, H] and topk_idx [T, K]")
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    _need(x, torch.bfloat16, "x")
+    _need(topk_idx, torch.int64, "topk_idx", (T, K))
+    _need(workspace, torch.uint8, "workspace")
+    dev = x.device
+    R = T * K
+    if out is None:
+        out = Dispatched(
+            torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev),
+            torch.empty((R, H // 128), dtype=torch.float32, device=dev) if fp8 else None,
+            torch.empty(R, dtype=torch.int32, device=dev),
+            torch.empty((T, K), dtype=torch.int32, device=dev))
+    _need(out.recv_x, torch.uint8 if fp8 else torch.bfloat16, "recv_x", (R, H))
+    if fp8:
+        _need(out.recv_scales, torch.float32, "recv_scales", (R, H // 128))
+    _need(out.recv_src_token, torch.int32, "recv_src_token", (R,))
+    _need(out.dst_row, torch.int32, "dst_row", (T, K))
+    _check(lib().ep_dispatch(
+        _ptr(x), T, H, _ptr(topk_idx), K, int(num_experts), int(num_partitions),
+        EP_DTYPE_FP8_E4M3 if fp8 else EP_DTYPE_BF16, _ptr(out.recv_x),
+        _ptr(out.recv_scales) if fp8 else None, _ptr(out.recv_src_token), _ptr(out.dst_row),
+        _ptr(workspace), workspace.numel(), _stream(x)), "ep_dispatch")
+    return out
+
+
+def combine(y: torch.Tensor, dst_row: torch.Tensor, topk_weights: torch.Tensor,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """ep_combine: y [R, H] bf16 expert outputs -> out [T, H] bf16."""
+    if y.dim() != 2 or dst_row.dim() != 2:
+        raise ValueError("y must be [R, H] and dst_row [T, K]")
+    T, K = dst_row.shape
+    H = y.shape[1]
+    _need(y, torch.bfloat16, "y")
+    _need(dst_row, torch.int32, "dst_row")
+    _need(topk_weights, torch.float32, "topk_weights", (T, K))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _need(out, torch.bfloat16, "out", (T, H))
+    _check(lib().ep_combine(_ptr(y), y.shape[0], _ptr(dst_row), _ptr(topk_weights), T, K, H,
+                            _ptr(out), _stream(y)), "ep_combine")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# diagnostics
+# ---------------------------------------------------------------------------
+
+def convert_e4m3(v: torch.Tensor, mode: int = 0) -> torch.Tensor:
+    """E4M3 codes of fp32 ``v`` with the dispatch kernel's conversion (mode 0)
+    or the software conversion (mode 1)."""
+    _need(v, torch.float32, "v")
+    out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    _check(lib().ep_convert_e4m3(_ptr(v), _ptr(out), v.numel(), mode, _stream(v)),
+           "ep_convert_e4m3")
+    return out
+
+
+def convert_bf16(v: torch.Tensor) -> torch.Tensor:
+    """bf16 bits (as int16) of fp32 ``v`` with the combine kernel's rounding."""
+    _need(v, torch.float32, "v")
+    out = torch.empty(v.shape, dtype=torch.int16, device=v.device)
+    _check(lib().ep_convert_bf16(_ptr(v), _ptr(out), v.numel(), _stream(v)), "ep_convert_bf16")
+    return out
+
+
+def copy(src: torch.Tensor, dst: torch.Tensor):
+    """ep_copy of all of ``src``'s bytes into ``dst``."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst too small")
+    _check(lib().ep_copy(_ptr(src), _ptr(dst), nbytes, _stream(src)), "ep_copy")

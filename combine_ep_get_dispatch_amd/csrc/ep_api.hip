@@ -1,0 +1,142 @@
+// C-ABI entry points (include/ep.h): host-side validation, workspace sizing
+// and kernel launches.  Nothing here touches the device before validation
+// has passed, and nothing here allocates.
+#include "ep.h"
+#include "ep_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxRows = (int64_t)1 << 31;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by the layout and dispatch calls.
+ep_status_t check_routing_shape(int32_t T, int32_t K, int32_t E, int32_t P) {
+    if (T < 0 || K <= 0 || E <= 0 || P <= 0) return EP_ERR_INVALID_ARG;
+    if (E % P != 0 || K > E) return EP_ERR_INVALID_ARG;
+    if ((int64_t)T * K >= kMaxRows) return EP_ERR_INVALID_ARG;
+    if (E > EP_MAX_EXPERTS || K > EP_MAX_TOPK) return EP_ERR_UNSUPPORTED;
+    return EP_OK;
+}
+
+ep_status_t from_hip(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t ep_workspace_bytes(int32_t num_tokens, int32_t num_topk, int32_t num_experts,
+                          int32_t num_partitions) {
+    if (check_routing_shape(num_tokens, num_topk, num_experts, num_partitions) != EP_OK)
+        return 0;
+    return ep::ws_map(num_tokens, num_topk, num_experts, num_partitions).total;
+}
+
+ep_status_t ep_get_dispatch_layout(const int64_t* topk_idx, int32_t num_tokens,
+                                   int32_t num_topk, int32_t num_experts,
+                                   int32_t num_partitions, int32_t* num_tokens_per_expert,
+                                   int32_t* num_tokens_per_partition,
+                                   uint8_t* is_token_in_partition, int32_t* expert_offsets,
+                                   int32_t* partition_offsets, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    const int32_t T = num_tokens, K = num_topk, E = num_experts, P = num_partitions;
+    ep_status_t st = check_routing_shape(T, K, E, P);
+    if (st != EP_OK) return st;
+    if (!num_tokens_per_expert || !num_tokens_per_partition || !expert_offsets ||
+        !partition_offsets || !workspace)
+        return EP_ERR_INVALID_ARG;
+    if (T > 0 && (!topk_idx || !is_token_in_partition)) return EP_ERR_INVALID_ARG;
+    const ep::WsMap m = ep::ws_map(T, K, E, P);
+    if (workspace_bytes < m.total) return EP_ERR_WORKSPACE;
+    return from_hip(ep::launch_layout(topk_idx, T, K, E, P, workspace, m, num_tokens_per_expert,
+                                      num_tokens_per_partition, is_token_in_partition,
+                                      expert_offsets, partition_offsets,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+ep_status_t ep_dispatch(const void* x, int32_t num_tokens, int32_t hidden,
+                        const int64_t* topk_idx, int32_t num_topk, int32_t num_experts,
+                        int32_t num_partitions, ep_dtype_t out_dtype, void* recv_x,
+                        float* recv_scales, int32_t* recv_src_token, int32_t* dst_row,
+                        const void* workspace, size_t workspace_bytes, void* stream) {
+    const int32_t T = num_tokens, H = hidden, K = num_topk, E = num_experts, P = num_partitions;
+    ep_status_t st = check_routing_shape(T, K, E, P);
+    if (st != EP_OK) return st;
+    if (out_dtype != EP_DTYPE_BF16 && out_dtype != EP_DTYPE_FP8_E4M3) return EP_ERR_INVALID_ARG;
+    const bool fp8 = out_dtype == EP_DTYPE_FP8_E4M3;
+    if (H <= 0 || H % 8 != 0 || (fp8 && H % 128 != 0)) return EP_ERR_INVALID_ARG;
+    if (!workspace) return EP_ERR_INVALID_ARG;
+    if (T > 0) {
+        if (!x || !topk_idx || !recv_x || !recv_src_token || !dst_row) return EP_ERR_INVALID_ARG;
+        if (fp8 && !recv_scales) return EP_ERR_INVALID_ARG;
+        if (!aligned16(x) || !aligned16(recv_x)) return EP_ERR_INVALID_ARG;
+    }
+    const ep::WsMap m = ep::ws_map(T, K, E, P);
+    if (workspace_bytes < m.total) return EP_ERR_WORKSPACE;
+    return from_hip(ep::launch_dispatch(static_cast<const uint16_t*>(x), T, H, topk_idx, K, E,
+                                        fp8, recv_x, recv_scales, recv_src_token, dst_row,
+                                        workspace, m, static_cast<hipStream_t>(stream)));
+}
+
+ep_status_t ep_combine(const void* y, int64_t num_rows, const int32_t* dst_row,
+                       const float* topk_weights, int32_t num_tokens, int32_t num_topk,
+                       int32_t hidden, void* out, void* stream) {
+    const int32_t T = num_tokens, K = num_topk, H = hidden;
+    if (T < 0 || K <= 0 || H <= 0 || H % 8 != 0 || num_rows < 0) return EP_ERR_INVALID_ARG;
+    if ((int64_t)T * K >= kMaxRows) return EP_ERR_INVALID_ARG;
+    if (K > EP_MAX_TOPK) return EP_ERR_UNSUPPORTED;
+    if (T > 0) {
+        if (!dst_row || !topk_weights || !out) return EP_ERR_INVALID_ARG;
+        if ((y && !aligned16(y)) || !aligned16(out)) return EP_ERR_INVALID_ARG;
+    }
+    if (T > 0 && num_rows > 0 && !y) return EP_ERR_INVALID_ARG;
+    return from_hip(ep::launch_combine(static_cast<const uint16_t*>(y), num_rows, dst_row,
+                                       topk_weights, T, K, H, static_cast<uint16_t*>(out),
+                                       static_cast<hipStream_t>(stream)));
+}
+
+ep_status_t ep_get_device_error(const void* workspace, size_t workspace_bytes,
+                                int64_t* num_invalid, void* stream) {
+    if (!workspace || !num_invalid || workspace_bytes < ep::kWsHeaderBytes)
+        return EP_ERR_INVALID_ARG;
+    const ep::WsHeader* hdr = static_cast<const ep::WsHeader*>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int64_t v = 0;
+    if (hipMemcpyAsync(&v, &hdr->invalid_published, sizeof v, hipMemcpyDeviceToHost, s) !=
+        hipSuccess)
+        return EP_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return EP_ERR_HIP;
+    *num_invalid = v;
+    return EP_OK;
+}
+
+const char* ep_status_string(ep_status_t status) {
+    switch (status) {
+        case EP_OK: return "EP_OK";
+        case EP_ERR_INVALID_ARG: return "EP_ERR_INVALID_ARG";
+        case EP_ERR_UNSUPPORTED: return "EP_ERR_UNSUPPORTED";
+        case EP_ERR_WORKSPACE: return "EP_ERR_WORKSPACE";
+        case EP_ERR_HIP: return "EP_ERR_HIP";
+    }
+    return "EP_ERR_UNKNOWN";
+}
+
+ep_status_t ep_convert_e4m3(const float* in, uint8_t* out, int64_t n, int32_t mode,
+                            void* stream) {
+    if (n < 0 || (n > 0 && (!in || !out)) || (mode != 0 && mode != 1)) return EP_ERR_INVALID_ARG;
+    return from_hip(ep::launch_convert_e4m3(in, out, n, mode, static_cast<hipStream_t>(stream)));
+}
+
+ep_status_t ep_convert_bf16(const float* in, uint16_t* out, int64_t n, void* stream) {
+    if (n < 0 || (n > 0 && (!in || !out))) return EP_ERR_INVALID_ARG;
+    return from_hip(ep::launch_convert_bf16(in, out, n, static_cast<hipStream_t>(stream)));
+}
+
+ep_status_t ep_copy(const void* src, void* dst, size_t bytes, void* stream) {
+    if (bytes % 16 != 0) return EP_ERR_INVALID_ARG;
+    if (bytes > 0 && (!src || !dst || !aligned16(src) || !aligned16(dst)))
+        return EP_ERR_INVALID_ARG;
+    return from_hip(ep::launch_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

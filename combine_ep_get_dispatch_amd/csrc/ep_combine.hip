@@ -1,0 +1,127 @@
+// Combine on gfx950: gather each token's expert outputs back from the
+// receive rows and reduce them with the token's gate weights,
+//   out[t,h] = bf16_rne( fma chain over k of w[t,k] * y[dst_row[t,k], h] ),
+// accumulated in fp32 from +0 in slot order, masked slots (dst_row < 0)
+// skipped.
+//
+// Combine is the second half of the expert-parallel all-to-all ("DeepSeek
+// releases DeepEP, an efficient communication library for MoE models",
+// section "DeepEP: Optimizing MoE Communication"); the weighting and the
+// accumulation order are this library's reading.
+//
+// Design.  The kernel is HBM-bound (about 1 flop per byte), so the goal is to
+// keep enough independent 16-byte loads in flight: one wave per (token,
+// 512-channel chunk), 8 channels per lane; lane k first fetches dst_row and
+// the weight of slot k, then every slot's 16-byte row segment is loaded
+// before the first FMA (K loads in flight per lane), and the result is
+// rounded with v_cvt_pk_bf16_f32 and written as one 16-byte store.  The slot
+// count is a template parameter for the common top-k values so the loads
+// unroll; other K take a loop over groups of 8 slots.
+#include "ep_internal.h"
+#include "ep_device.h"
+
+namespace ep {
+namespace {
+
+__device__ __forceinline__ void fma8(float (&acc)[8], float w, const uint4& v) {
+    acc[0] = __builtin_fmaf(w, bf16_lo(v.x), acc[0]);
+    acc[1] = __builtin_fmaf(w, bf16_hi(v.x), acc[1]);
+    acc[2] = __builtin_fmaf(w, bf16_lo(v.y), acc[2]);
+    acc[3] = __builtin_fmaf(w, bf16_hi(v.y), acc[3]);
+    acc[4] = __builtin_fmaf(w, bf16_lo(v.z), acc[4]);
+    acc[5] = __builtin_fmaf(w, bf16_hi(v.z), acc[5]);
+    acc[6] = __builtin_fmaf(w, bf16_lo(v.w), acc[6]);
+    acc[7] = __builtin_fmaf(w, bf16_hi(v.w), acc[7]);
+}
+
+// Slots [k0, k0 + KN) of the token: load all, then accumulate in order.
+template <int KN>
+__device__ __forceinline__ void combine_slots(float (&acc)[8], const uint16_t* __restrict__ y,
+                                              int H, int h0, bool act, int drow, float wl,
+                                              int k0, int kend) {
+    uint4 v[KN];
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+        const int d = __builtin_amdgcn_readlane(drow, k0 + i);
+        v[i] = make_uint4(0, 0, 0, 0);
+        if (k0 + i < kend && d >= 0 && act)
+            v[i] = *reinterpret_cast<const uint4*>(y + (int64_t)d * H + h0);
+    }
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+        const int d = __builtin_amdgcn_readlane(drow, k0 + i);
+        const float w = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), k0 + i));
+        if (k0 + i < kend && d >= 0) fma8(acc, w, v[i]);
+    }
+}
+
+template <int KT>   // KT > 0: exactly KT slots; KT == 0: any K <= 64
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+    const uint16_t* __restrict__ y, int64_t nrows, const int32_t* __restrict__ dst_row,
+    const float* __restrict__ w, int K, int H, uint16_t* __restrict__ out, int nchunk,
+    int64_t ntask) {
+    const int lane = threadIdx.x & 63;
+    const int64_t task = (int64_t)blockIdx.x * (kCombineThreads / 64) +
+                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (task >= ntask) return;
+    const int t = (int)(task / nchunk);
+    const int c = (int)(task - (int64_t)t * nchunk);
+    const int h0 = c * kCombineChunk + lane * 8;
+    const bool act = h0 < H;
+
+    const int kk = KT > 0 ? KT : K;
+    int drow = -1;
+    float wl = 0.0f;
+    if (lane < kk) {
+        drow = dst_row[(int64_t)t * kk + lane];
+        wl = w[(int64_t)t * kk + lane];
+        if (drow >= nrows) drow = -1;   // outside y: skipped like a masked slot
+    }
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    if constexpr (KT > 0) {
+        combine_slots<KT>(acc, y, H, h0, act, drow, wl, 0, KT);
+    } else {
+        for (int k0 = 0; k0 < K; k0 += 8) combine_slots<8>(acc, y, H, h0, act, drow, wl, k0, K);
+    }
+    if (act) {
+        uint4 o;
+        o.x = pack_bf16x2(acc[0], acc[1]);
+        o.y = pack_bf16x2(acc[2], acc[3]);
+        o.z = pack_bf16x2(acc[4], acc[5]);
+        o.w = pack_bf16x2(acc[6], acc[7]);
+        *reinterpret_cast<uint4*>(out + (int64_t)t * H + h0) = o;
+    }
+}
+
+template <int KT>
+void launch_k(dim3 grid, hipStream_t s, const uint16_t* y, int64_t nrows,
+              const int32_t* dst_row, const float* w, int K, int H, uint16_t* out, int nchunk,
+              int64_t ntask) {
+    hipLaunchKernelGGL(combine_kernel<KT>, grid, dim3(kCombineThreads), 0, s, y, nrows, dst_row,
+                       w, K, H, out, nchunk, ntask);
+}
+
+}  // namespace
+
+hipError_t launch_combine(const uint16_t* y, int64_t nrows, const int32_t* dst_row,
+                          const float* w, int T, int K, int H, uint16_t* out, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const int nchunk = (H + kCombineChunk - 1) / kCombineChunk;
+    const int64_t ntask = (int64_t)T * nchunk;
+    const int wpb = kCombineThreads / 64;
+    const dim3 grid((unsigned)((ntask + wpb - 1) / wpb));
+    switch (K) {
+        case 1: launch_k<1>(grid, s, y, nrows, dst_row, w, K, H, out, nchunk, ntask); break;
+        case 2: launch_k<2>(grid, s, y, nrows, dst_row, w, K, H, out, nchunk, ntask); break;
+        case 4: launch_k<4>(grid, s, y, nrows, dst_row, w, K, H, out, nchunk, ntask); break;
+        case 6: launch_k<6>(grid, s, y, nrows, dst_row, w, K, H, out, nchunk, ntask); break;
+        case 8: launch_k<8>(grid, s, y, nrows, dst_row, w, K, H, out, nchunk, ntask); break;
+        default: launch_k<0>(grid, s, y, nrows, dst_row, w, K, H, out, nchunk, ntask); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace ep

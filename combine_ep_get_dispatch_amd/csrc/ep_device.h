@@ -1,0 +1,68 @@
+// Device-side helpers for the gfx950 kernels: bf16 unpacking, the fp32 ->
+// OCP E4M3 and fp32 -> bf16 conversions, and wave-level reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ep {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 word.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> two bf16 (round to nearest even) packed low/high, with gfx950's
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    bf16x2 b = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+// Four fp32 -> four OCP E4M3 codes packed into a dword (byte i = value i),
+// with gfx950's v_cvt_pk_fp8_f32: round to nearest even.  Inputs of the
+// quantiser never exceed 448 * (1 + 2^-23) in magnitude, which rounds to 448,
+// so the instruction's out-of-range behaviour is never reached there.
+__device__ __forceinline__ uint32_t e4m3x4_hw(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+// Bit-level fp32 -> OCP E4M3, round to nearest even, saturating to +-448,
+// sign kept, NaN -> S.1111.111.  Normal results keep the top 3 fp32 mantissa
+// bits after rounding the 20 dropped bits to nearest even (a carry moves into
+// the exponent); results below 2^-6 are multiples of 2^-9, found by scaling
+// by 2^9 (exact) and rounding to an integer.
+__device__ __forceinline__ uint32_t e4m3_sw(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return sign | 0x7fu;           // NaN
+    if (a >= 0x43e00000u) return sign | 0x7eu;          // |v| >= 448
+    if (a < 0x3c800000u) {                              // |v| < 2^-6
+        const float q = __builtin_rintf(__uint_as_float(a) * 512.0f);
+        return sign | (uint32_t)q;                      // 0..8 (8 = 2^-6)
+    }
+    const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+    uint32_t code = r - ((127u - 7u) << 3);
+    if (code > 0x7eu) code = 0x7eu;
+    return sign | code;
+}
+
+__device__ __forceinline__ uint32_t e4m3x4_sw(float a, float b, float c, float d) {
+    return e4m3_sw(a) | (e4m3_sw(b) << 8) | (e4m3_sw(c) << 16) | (e4m3_sw(d) << 24);
+}
+
+// Maximum over the 8 lanes of an aligned group of 8 (lanes 8g .. 8g+7).
+__device__ __forceinline__ float group8_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 1));
+    v = fmaxf(v, __shfl_xor(v, 2));
+    v = fmaxf(v, __shfl_xor(v, 4));
+    return v;
+}
+
+}  // namespace ep

@@ -1,0 +1,86 @@
+// Internal interface between the C-ABI entry points (ep_api.hip) and the
+// gfx950 kernels.  Not installed; the public interface is include/ep.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ep {
+
+// ---------------------------------------------------------------- layout ---
+// The layout kernel gives each workgroup one block of consecutive tokens
+// holding about kLayoutEntries (token, slot) entries, split over 8 waves.
+constexpr int kLayoutThreads = 512;
+constexpr int kLayoutWaves = kLayoutThreads / 64;
+constexpr int kLayoutEntries = 2048;
+
+__host__ __device__ inline int layout_tokens_per_block(int K) {
+    int tb = kLayoutEntries / K;
+    return tb < 1 ? 1 : tb;
+}
+
+// First 256 bytes of the caller's workspace.  `ticket`, `invalid_accum` are
+// zero between calls: the last layout workgroup resets them.
+struct WsHeader {
+    uint32_t ticket;            // workgroups of the current layout launch that finished
+    int32_t num_valid;          // N = valid slots of the last layout
+    int64_t invalid_accum;      // invalid slots counted by the running launch
+    int64_t invalid_published;  // invalid slots of the last completed layout
+};
+constexpr size_t kWsHeaderBytes = 256;
+static_assert(sizeof(WsHeader) <= kWsHeaderBytes, "header too large");
+
+// Workspace map for one shape (offsets in bytes from the workspace start):
+//   [0, 256)        WsHeader
+//   cnt  int32 [E][nb]   per-block expert counts, then (in place) per-block
+//                        bases: expert_offsets[e] + rows of e in earlier blocks
+//   pcnt int32 [P][nb]   per-block distinct-token counts per partition
+//   rank int32 [T*K]     rank of each slot among the earlier slots of its
+//                        expert inside its block (-1 if masked/invalid)
+struct WsMap {
+    int nb = 0;        // token blocks
+    int tb = 1;        // tokens per block
+    size_t cnt_off = 0, pcnt_off = 0, rank_off = 0, total = 0;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+inline WsMap ws_map(int T, int K, int E, int P) {
+    WsMap m;
+    m.tb = layout_tokens_per_block(K);
+    m.nb = (T + m.tb - 1) / m.tb;
+    m.cnt_off = kWsHeaderBytes;
+    m.pcnt_off = m.cnt_off + align256(sizeof(int32_t) * (size_t)E * (size_t)m.nb);
+    m.rank_off = m.pcnt_off + align256(sizeof(int32_t) * (size_t)P * (size_t)m.nb);
+    m.total = m.rank_off + align256(sizeof(int32_t) * (size_t)T * (size_t)K);
+    return m;
+}
+
+hipError_t launch_layout(const int64_t* idx, int T, int K, int E, int P, void* ws,
+                         const WsMap& m, int32_t* cnt_e, int32_t* cnt_p, uint8_t* in_part,
+                         int32_t* off_e, int32_t* off_p, hipStream_t s);
+
+// ---------------------------------------------------------------- dispatch --
+// One wave per (token, 1024-channel chunk); 16 channels per lane.
+constexpr int kDispatchThreads = 256;
+constexpr int kDispatchChunk = 1024;
+
+hipError_t launch_dispatch(const uint16_t* x, int T, int H, const int64_t* idx, int K, int E,
+                           bool fp8, void* recv_x, float* recv_scales, int32_t* recv_src,
+                           int32_t* dst_row, const void* ws, const WsMap& m, hipStream_t s);
+
+// ---------------------------------------------------------------- combine ---
+// One wave per (token, 512-channel chunk); 8 channels per lane.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineChunk = 512;
+
+hipError_t launch_combine(const uint16_t* y, int64_t nrows, const int32_t* dst_row,
+                          const float* w, int T, int K, int H, uint16_t* out, hipStream_t s);
+
+// ------------------------------------------------------------ diagnostics ---
+hipError_t launch_convert_e4m3(const float* in, uint8_t* out, int64_t n, int mode, hipStream_t s);
+hipError_t launch_convert_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
+}  // namespace ep

@@ -1,0 +1,186 @@
+/*
+ * ep.h -- C ABI of the MoE token dispatch / combine library for AMD MI355X
+ * (gfx950, CDNA4).  Built as libep_mi355x.so from hand-written HIP kernels.
+ *
+ * The operations.  In expert parallelism every token is sent to the experts
+ * its router picked ("dispatch") and the experts' outputs are brought back to
+ * the token ("combine"); the two form an all-to-all exchange between the GPUs
+ * that host the experts ("DeepSeek releases DeepEP, an efficient communication
+ * library for MoE models", section "DeepEP: Optimizing MoE Communication").
+ * Dispatch may carry FP8 payloads (FP8 for dispatch is in the feature list of
+ * "DeepSeek Open Source Weekly Review - 2").  This library computes one GPU's
+ * share of that exchange with the destination partitions laid out as
+ * contiguous runs of one local receive buffer, so that partition p's rows are
+ * exactly what would be sent to GPU p.
+ *
+ * Notation: T tokens, H hidden size, K router slots per token (top-k),
+ * E experts, P destination partitions (E % P == 0; expert e belongs to
+ * partition e / (E/P)), G = H/128 scale groups, R = T*K receive rows.
+ *
+ * Conventions shared by every entry point:
+ *  - Array arguments are device pointers on the current HIP device, row-major
+ *    and contiguous, owned by the caller.  The library never allocates or
+ *    frees memory; apart from the caller's workspace it keeps no state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued asynchronously; nothing synchronises except
+ *    ep_get_device_error.
+ *  - Arguments are validated on the host; on any error the call returns a
+ *    non-zero ep_status_t and enqueues nothing.  EP_ERR_HIP reports a failed
+ *    launch (hipGetLastError after the launch).
+ *  - Buffers must not overlap.  x, recv_x, y and out must be 16-byte aligned.
+ *  - topk_idx entries: a value in [0, E) selects that expert; -1 is a masked
+ *    slot (skipped everywhere); any other value is an invalid slot: it is
+ *    skipped like a masked one and counted in the workspace's error word
+ *    (see ep_get_device_error).
+ */
+#ifndef EP_MI355X_H
+#define EP_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EP_OK = 0,
+    EP_ERR_INVALID_ARG = 1,  /* null pointer, bad size or inconsistent shape */
+    EP_ERR_UNSUPPORTED = 2,  /* valid but outside this build's limits       */
+    EP_ERR_WORKSPACE = 3,    /* workspace smaller than ep_workspace_bytes() */
+    EP_ERR_HIP = 4           /* a HIP call or kernel launch failed          */
+} ep_status_t;
+
+typedef enum {
+    EP_DTYPE_BF16 = 0,       /* receive rows are bf16 copies of the tokens  */
+    EP_DTYPE_FP8_E4M3 = 1    /* receive rows are OCP E4M3 codes + scales    */
+} ep_dtype_t;
+
+/* Limits of this build (EP_ERR_UNSUPPORTED beyond them). */
+#define EP_MAX_EXPERTS 1024
+#define EP_MAX_TOPK 64
+
+/*
+ * Bytes of device workspace that ep_get_dispatch_layout and ep_dispatch need
+ * for this shape; 0 if the shape is invalid.  The first 256 bytes of a fresh
+ * workspace must be zero (allocate it zero-filled once); every layout call
+ * leaves them zero again, so the same workspace can serve any number of calls
+ * and any shape up to its size.  One workspace serves one stream at a time.
+ */
+size_t ep_workspace_bytes(int32_t num_tokens, int32_t num_topk, int32_t num_experts,
+                          int32_t num_partitions);
+
+/*
+ * Dispatch layout: the counts and offsets that the all-to-all needs before
+ * any data moves (the bookkeeping behind the exchange of "DeepEP: Optimizing
+ * MoE Communication"; the pages do not spell it out, the definitions below
+ * are this library's):
+ *   num_tokens_per_expert    [E]   valid slots routed to expert e
+ *   num_tokens_per_partition [P]   distinct tokens with a valid slot in p
+ *   is_token_in_partition  [T*P]   uint8, 1 iff token t has a valid slot in p
+ *   expert_offsets         [E+1]   exclusive prefix sum of the expert counts;
+ *                                  expert_offsets[E] = N = number of valid slots
+ *   partition_offsets      [P+1]   expert_offsets[p * (E/P)]: partition p owns
+ *                                  receive rows [partition_offsets[p],
+ *                                  partition_offsets[p+1])
+ * It also records, in the workspace, each slot's rank among the earlier slots
+ * of the same expert (token-major, then slot order) and per-block bases, which
+ * ep_dispatch turns into receive rows.  topk_idx is int64 [T*K].
+ * T may be 0 (all counts and offsets become 0).
+ */
+ep_status_t ep_get_dispatch_layout(const int64_t *topk_idx, int32_t num_tokens,
+                                   int32_t num_topk, int32_t num_experts,
+                                   int32_t num_partitions,
+                                   int32_t *num_tokens_per_expert,
+                                   int32_t *num_tokens_per_partition,
+                                   uint8_t *is_token_in_partition,
+                                   int32_t *expert_offsets, int32_t *partition_offsets,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Dispatch (the "dispatch" half of "DeepEP: Optimizing MoE Communication"):
+ * every valid slot (t,k) gets its own receive row
+ *   dst_row[t*K+k] = expert_offsets[e] + (rank of (t,k) among the slots of
+ *                    expert e, in token-major then slot order),  e = topk_idx
+ * or -1 for a masked/invalid slot, and recv_src_token[dst_row] = t; receive
+ * rows r >= N get recv_src_token[r] = -1 and their recv_x/recv_scales rows are
+ * left untouched.  (A row the workspace would place outside [0, R) -- only
+ * possible when the workspace does not come from the matching layout call --
+ * is dropped and its slot reported as -1, so no write leaves the buffers.)  Rows are therefore grouped by expert in ascending order and
+ * partition p's rows are one contiguous run.
+ *   out_dtype == EP_DTYPE_BF16:  recv_x is bf16 [R*H], row r a bitwise copy of
+ *     x[recv_src_token[r]]; recv_scales is ignored (may be NULL).
+ *   out_dtype == EP_DTYPE_FP8_E4M3 (H % 128 == 0): for each token and each
+ *     group of 128 consecutive channels, a = max|x|, a_c = max(a, 1e-4f),
+ *     s = a_c / 448 and the codes are E4M3(x * (448 / a_c)) (OCP E4M3, round
+ *     to nearest even, saturating, sign kept); recv_x is uint8 [R*H] and
+ *     recv_scales fp32 [R*G] holds s, so x ~= code * s.  (FP8 for dispatch:
+ *     feature list of "DeepSeek Open Source Weekly Review - 2"; the format,
+ *     granularity and scale rule are this library's.)
+ * x is bf16 [T*H]; topk_idx int64 [T*K] and workspace must be the ones the
+ * preceding ep_get_dispatch_layout call used, with the same T, K, E, P and on
+ * the same stream (or ordered after it).  H % 8 == 0.
+ */
+ep_status_t ep_dispatch(const void *x, int32_t num_tokens, int32_t hidden,
+                        const int64_t *topk_idx, int32_t num_topk, int32_t num_experts,
+                        int32_t num_partitions, ep_dtype_t out_dtype,
+                        void *recv_x, float *recv_scales, int32_t *recv_src_token,
+                        int32_t *dst_row, const void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/*
+ * Combine (the "combine" half of "DeepEP: Optimizing MoE Communication"):
+ * bring each token's expert outputs back and reduce them with its gate
+ * weights.  For every token t and channel h:
+ *   acc = +0.0f;  for k = 0..K-1 with 0 <= dst_row[t*K+k] < num_rows:
+ *       acc = fmaf(topk_weights[t*K+k], y[dst_row[t*K+k]*H + h], acc)
+ *   out[t*H + h] = bf16(acc), rounded to nearest even.
+ * y is bf16 [num_rows * H] (normally num_rows = T*K, the receive rows in
+ * dispatch's order); dst_row int32 [T*K] as written by ep_dispatch; slots
+ * whose dst_row lies outside [0, num_rows) are skipped like masked ones, so
+ * no y row outside the buffer is ever read.  topk_weights fp32 [T*K]; out
+ * bf16 [T*H].  H % 8 == 0.  T may be 0.  (The weighting and the fp32
+ * accumulation order are this library's reading; the pages only name the
+ * operation.)
+ */
+ep_status_t ep_combine(const void *y, int64_t num_rows, const int32_t *dst_row,
+                       const float *topk_weights, int32_t num_tokens, int32_t num_topk,
+                       int32_t hidden, void *out, void *stream);
+
+/*
+ * Waits for `stream`, then stores in *num_invalid the number of invalid
+ * topk_idx entries (not -1 and outside [0, E)) that the most recent
+ * ep_get_dispatch_layout on this workspace met.  num_invalid is a host
+ * pointer.
+ */
+ep_status_t ep_get_device_error(const void *workspace, size_t workspace_bytes,
+                                int64_t *num_invalid, void *stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *ep_status_string(ep_status_t status);
+
+/*
+ * Diagnostics and measurement helpers.  They run the same device code as the
+ * path above, so tests can check it value by value and benchmarks can
+ * calibrate counters against a kernel of known traffic.
+ */
+
+/* out[i] = E4M3 code of in[i], with the conversion ep_dispatch uses (mode 0)
+ * or the bit-exact software conversion (mode 1).  in fp32 [n], out uint8 [n]. */
+ep_status_t ep_convert_e4m3(const float *in, uint8_t *out, int64_t n, int32_t mode,
+                            void *stream);
+
+/* out[i] = bf16 bits of in[i], rounded to nearest even, with the conversion
+ * ep_combine uses.  in fp32 [n], out uint16 [n]. */
+ep_status_t ep_convert_bf16(const float *in, uint16_t *out, int64_t n, void *stream);
+
+/* Plain streaming copy of `bytes` bytes (multiple of 16, 16-byte aligned
+ * pointers): reads `bytes` and writes `bytes`.  Used as the reference kernel
+ * for HBM traffic counters and the measured copy ceiling. */
+ep_status_t ep_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_MI355X_H */

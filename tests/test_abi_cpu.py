@@ -1,0 +1,165 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/ep.h declares, sizes workspaces, and rejects bad arguments on the host
+before anything is enqueued.
+
+No call here reaches a kernel: each one must fail host validation.  When a
+GPU is present the pointers are real (tiny) device buffers, so that even a
+validation bug could not hand a kernel a bogus address; without one they are
+aligned placeholders that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from combine_ep_get_dispatch_amd import binding as b
+from combine_ep_get_dispatch_amd import build as build_mod
+
+HEADER = os.path.join(build_mod.INCLUDE, "ep.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"ep_get_dispatch_layout", "ep_dispatch", "ep_combine"} <= set(names)
+    lib = ctypes.CDLL(b.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the binding declares a signature for each of them
+    assert set(names) == set(b.SIGNATURES), set(names) ^ set(b.SIGNATURES)
+
+
+def test_status_strings():
+    for code, name in [(0, "EP_OK"), (1, "EP_ERR_INVALID_ARG"), (2, "EP_ERR_UNSUPPORTED"),
+                       (3, "EP_ERR_WORKSPACE"), (4, "EP_ERR_HIP"), (99, "EP_ERR_UNKNOWN")]:
+        assert b.status_string(code) == name
+
+
+def test_workspace_bytes():
+    L = b.lib()
+    # header + cnt [E][nb] + pcnt [P][nb] + rank [T*K], each rounded up to 256 bytes
+    tb = 2048 // 8
+    nb = -(-4096 // tb)
+    r256 = lambda v: -(-v // 256) * 256
+    want = 256 + r256(4 * 256 * nb) + r256(4 * 64 * nb) + r256(4 * 4096 * 8)
+    assert L.ep_workspace_bytes(4096, 8, 256, 64) == want
+    assert L.ep_workspace_bytes(0, 8, 256, 64) == 256
+    for bad in [(-1, 2, 4, 2), (4, 0, 4, 2), (4, 2, 0, 1), (4, 2, 4, 0), (4, 2, 6, 4),
+                (4, 5, 4, 2), (1 << 28, 8, 256, 64), (4, 2, 2048, 2), (4, 65, 128, 2)]:
+        assert L.ep_workspace_bytes(*bad) == 0, bad
+
+
+class Bufs:
+    """Device buffers (GPU present) or never-dereferenced placeholders."""
+
+    def __init__(self):
+        self.keep = []
+        self.gpu = torch.cuda.is_available()
+
+    def __call__(self, nbytes=4096):
+        if self.gpu:
+            t = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+            self.keep.append(t)
+            return ctypes.c_void_p(t.data_ptr())
+        return ctypes.c_void_p(0x100000)
+
+
+@pytest.fixture
+def buf():
+    return Bufs()
+
+
+def test_layout_rejects_bad_arguments(buf):
+    L = b.lib()
+    ws = buf(1 << 16)
+    p = [buf() for _ in range(6)]
+
+    def call(idx=p[0], T=4, K=2, E=4, P=2, ce=p[1], cp=p[2], ip=p[3], oe=p[4], op=p[5],
+             w=ws, wsz=1 << 16):
+        return L.ep_get_dispatch_layout(idx, T, K, E, P, ce, cp, ip, oe, op, w, wsz, None)
+
+    assert call(idx=None) == INVALID
+    assert call(ce=None) == INVALID
+    assert call(cp=None) == INVALID
+    assert call(ip=None) == INVALID
+    assert call(oe=None) == INVALID
+    assert call(op=None) == INVALID
+    assert call(w=None) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(K=0) == INVALID
+    assert call(E=0) == INVALID
+    assert call(P=0) == INVALID
+    assert call(E=6, P=4) == INVALID          # E % P != 0
+    assert call(K=5) == INVALID               # K > E
+    assert call(T=1 << 28, K=8, E=8) == INVALID   # T*K >= 2^31
+    assert call(E=2048, P=2) == UNSUPPORTED
+    assert call(K=65, E=128) == UNSUPPORTED
+    assert call(wsz=255) == WORKSPACE
+    assert call(T=4096, K=8, E=256, P=64, wsz=1 << 16) == WORKSPACE
+
+
+def test_dispatch_rejects_bad_arguments(buf):
+    L = b.lib()
+    ws = buf(1 << 16)
+    x, idx, rx, rs, src, dst = (buf() for _ in range(6))
+
+    def call(x=x, T=4, H=256, idx=idx, K=2, E=4, P=2, dt=0, rx=rx, rs=rs, src=src, dst=dst,
+             w=ws, wsz=1 << 16):
+        return L.ep_dispatch(x, T, H, idx, K, E, P, dt, rx, rs, src, dst, w, wsz, None)
+
+    for kw in [dict(x=None), dict(idx=None), dict(rx=None), dict(src=None), dict(dst=None),
+               dict(w=None), dict(H=0), dict(H=12), dict(dt=2), dict(dt=1, H=136),
+               dict(dt=1, rs=None), dict(E=6, P=4), dict(K=5), dict(T=-3),
+               dict(x=ctypes.c_void_p(0x100008)), dict(rx=ctypes.c_void_p(0x100004))]:
+        assert call(**kw) == INVALID, kw
+    assert call(E=2048, P=2) == UNSUPPORTED
+    assert call(wsz=128) == WORKSPACE
+
+
+def test_combine_rejects_bad_arguments(buf):
+    L = b.lib()
+    y, dst, w, out = (buf() for _ in range(4))
+
+    def call(y=y, rows=8, dst=dst, w=w, T=4, K=2, H=256, out=out):
+        return L.ep_combine(y, rows, dst, w, T, K, H, out, None)
+
+    for kw in [dict(y=None), dict(rows=-1), dict(dst=None), dict(w=None), dict(out=None),
+               dict(T=-1),
+               dict(K=0), dict(H=0), dict(H=20), dict(T=1 << 28, K=8),
+               dict(y=ctypes.c_void_p(0x100002)), dict(out=ctypes.c_void_p(0x10000c))]:
+        assert call(**kw) == INVALID, kw
+    assert call(K=65) == UNSUPPORTED
+
+
+def test_diagnostics_reject_bad_arguments(buf):
+    L = b.lib()
+    a, o = buf(), buf()
+    assert L.ep_convert_e4m3(None, o, 4, 0, None) == INVALID
+    assert L.ep_convert_e4m3(a, o, -1, 0, None) == INVALID
+    assert L.ep_convert_e4m3(a, o, 4, 2, None) == INVALID
+    assert L.ep_convert_bf16(a, None, 4, None) == INVALID
+    assert L.ep_copy(a, o, 17, None) == INVALID
+    assert L.ep_copy(None, o, 16, None) == INVALID
+    assert L.ep_copy(ctypes.c_void_p(0x100004), o, 16, None) == INVALID
+    n = ctypes.c_int64(0)
+    assert L.ep_get_device_error(None, 256, ctypes.byref(n), None) == INVALID
+    assert L.ep_get_device_error(a, 16, ctypes.byref(n), None) == INVALID
+    assert L.ep_get_device_error(a, 256, None, None) == INVALID
+
+
+def test_binding_rejects_cpu_tensors():
+    idx = torch.zeros((4, 2), dtype=torch.int64)
+    with pytest.raises(ValueError):
+        b.get_dispatch_layout(idx, 4, 2)
+    with pytest.raises((ValueError, TypeError)):
+        b.combine(torch.zeros((8, 16), dtype=torch.bfloat16),
+                  torch.zeros((4, 2), dtype=torch.int32), torch.zeros((4, 2)))

@@ -1,0 +1,134 @@
+"""Parity of the HIP path with the CPU oracle (GPU).
+
+Every case runs layout -> dispatch -> combine through the C ABI on cuda:0 and
+through the oracle on the same seeded inputs, and compares element by element
+(bit-exact layout, permutation, receive rows and FP8 scales; combine within
+2 bf16 ulp).  The five workload configurations run at their full sizes, in
+the same launch configuration the benchmark times; the generic cases cover
+ragged token blocks (T not a multiple of the layout block), ragged channel
+chunks (H not a multiple of 512/1024), masked, invalid and repeated expert
+ids, and the degenerate shapes (T = 0, one token, one expert, P = 1, P = E,
+K = E, everything routed to one expert, the largest E and K).
+"""
+import numpy as np
+import pytest
+import torch
+
+from combine_ep_get_dispatch_amd import binding as ep
+from combine_ep_get_dispatch_amd import workloads as wl
+from parity import announce, check_case, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skewed", "coarse"])
+def test_configuration_full_size(name):
+    case = wl.make(name)
+    stats = check_case(case, label="config " + name)
+    assert stats["N"] == case.T * case.K
+
+
+GENERIC = [
+    # T, H, E, P, K, seed, kwargs
+    (1000, 264, 16, 4, 3, 1, dict()),                       # ragged T and H (bf16)
+    (777, 1032, 64, 8, 6, 2, dict(masked_frac=0.1)),
+    (513, 384, 32, 4, 4, 3, dict(fp8=True)),                 # FP8, ragged T
+    (300, 1152, 256, 64, 8, 4, dict(fp8=True, masked_frac=0.05)),
+    (2500, 520, 8, 8, 2, 5, dict(skew=2.0)),
+    (96, 7168, 256, 32, 8, 6, dict(fp8=True, skew=1.5)),
+    (130, 136, 12, 3, 5, 7, dict(allow_dup=True)),           # repeated experts in a row
+    (257, 2048, 128, 16, 16, 8, dict(fp8=True)),            # generic-K combine path
+    (65, 512, 40, 5, 7, 9, dict(masked_frac=0.3, invalid_frac=0.1)),
+    (4097, 128, 1024, 1024, 64, 10, dict()),                 # largest E, P = E, largest K
+    (1, 8, 4, 2, 2, 11, dict()),                             # one token, smallest H
+    (50, 256, 1, 1, 1, 12, dict()),                          # a single expert
+    (200, 640, 16, 1, 16, 13, dict(fp8=True)),               # P = 1 and K = E
+    (100_000, 16, 4, 2, 1, 14, dict()),                      # many tokens, K = 1
+]
+
+
+@pytest.mark.parametrize("T,H,E,P,K,seed,kw", GENERIC,
+                         ids=["T%d_H%d_E%d_P%d_K%d" % g[:5] for g in GENERIC])
+def test_generic_case(T, H, E, P, K, seed, kw):
+    case = wl.random_case(T, H, E, P, K, seed, **kw)
+    check_case(case, label="random seed=%d" % seed)
+
+
+def test_all_tokens_to_one_expert():
+    case = wl.random_case(3000, 256, 32, 8, 1, 21)
+    case.topk_idx[:] = 17
+    check_case(case, label="one hot expert")
+
+
+def test_every_slot_masked():
+    case = wl.random_case(300, 256, 16, 4, 4, 22)
+    case.topk_idx[:] = -1
+    stats = check_case(case, label="all masked")
+    assert stats["N"] == 0
+
+
+def test_invalid_ids_are_counted():
+    case = wl.random_case(900, 128, 64, 8, 4, 23, invalid_frac=0.05, masked_frac=0.05)
+    n_bad = int(((case.topk_idx != -1) & ((case.topk_idx < 0) | (case.topk_idx >= 64))).sum())
+    assert n_bad > 0
+    g = run_gpu(case)
+    assert g["num_invalid"] == n_bad
+    check_case(case, label="invalid ids")
+
+
+def test_zero_tokens():
+    announce("zero tokens")
+    idx = torch.zeros((0, 4), dtype=torch.int64, device="cuda")
+    x = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda")
+    lay = ep.get_dispatch_layout(idx, 16, 4)
+    d = ep.dispatch(x, idx, 16, 4, lay.workspace, fp8=True)
+    out = ep.combine(torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda"), d.dst_row,
+                     torch.zeros((0, 4), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    assert out.shape == (0, 256)
+    assert lay.expert_offsets.cpu().tolist() == [0] * 17
+    assert lay.partition_offsets.cpu().tolist() == [0] * 5
+    assert lay.num_tokens_per_expert.sum().item() == 0
+    assert ep.get_device_error(lay.workspace) == 0
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace serves a large call, then smaller ones (its header must be
+    left clean by every layout call), then the large one again."""
+    big = wl.random_case(5000, 256, 64, 16, 8, 31, invalid_frac=0.01)
+    small = wl.random_case(37, 512, 16, 4, 2, 32, fp8=True)
+    ws = ep.new_workspace(5000, 8, 64, 16)
+    from parity import compare, run_oracle
+    for case in [big, small, small, big]:
+        announce("workspace reuse T=%d" % case.T)
+        g = run_gpu(case, workspace=ws)
+        compare(g, run_oracle(case), case)
+
+
+def test_deterministic_across_runs():
+    case = wl.make("decode")
+    announce("determinism decode")
+    a = run_gpu(case)
+    b = run_gpu(case)
+    for k in a:
+        np.testing.assert_array_equal(np.asarray(a[k]), np.asarray(b[k]), err_msg=k)
+
+
+def test_rows_past_the_valid_ones_are_untouched():
+    """Receive rows >= N are not written (dispatch leaves them as they were)."""
+    case = wl.random_case(400, 256, 16, 4, 4, 41, masked_frac=0.25)
+    announce("untouched rows")
+    idx = torch.from_numpy(case.topk_idx).cuda()
+    x = torch.from_numpy(case.x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    lay = ep.get_dispatch_layout(idx, case.E, case.P)
+    R = case.T * case.K
+    out = ep.Dispatched(torch.full((R, case.H), 0x1234, dtype=torch.int16,
+                                   device="cuda").view(torch.bfloat16),
+                        None, torch.empty(R, dtype=torch.int32, device="cuda"),
+                        torch.empty((case.T, case.K), dtype=torch.int32, device="cuda"))
+    ep.dispatch(x, idx, case.E, case.P, lay.workspace, out=out)
+    N = int(lay.expert_offsets[-1].item())
+    assert N < R
+    tail = out.recv_x[N:].view(torch.int16).cpu().numpy()
+    assert (tail == 0x1234).all()
+    assert (out.recv_src_token[N:].cpu().numpy() == -1).all()
