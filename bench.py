@@ -97,7 +97,7 @@ def cpu_baseline(wl_case, nbytes, seconds):
         t_total += time.perf_counter() - t0
         passes += 1
         log("cpu oracle pass %d: %.2f s total" % (passes, t_total))
-        if t_total >= seconds or passes >= 5:
+        if t_total >= seconds or passes >= 40:
             break
     return {"value": round(nbytes * passes / t_total / 1e9, 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle",

@@ -73,9 +73,9 @@ ep_status_t ep_dispatch(const void* x, int32_t num_tokens, int32_t hidden,
     }
     const ep::WsMap m = ep::ws_map(T, K, E, P);
     if (workspace_bytes < m.total) return EP_ERR_WORKSPACE;
-    return from_hip(ep::launch_dispatch(static_cast<const uint16_t*>(x), T, H, topk_idx, K, E,
-                                        fp8, recv_x, recv_scales, recv_src_token, dst_row,
-                                        workspace, m, static_cast<hipStream_t>(stream)));
+    return from_hip(ep::launch_dispatch(static_cast<const uint16_t*>(x), T, H, K, fp8, recv_x,
+                                        recv_scales, recv_src_token, dst_row, workspace, m,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 ep_status_t ep_combine(const void* y, int64_t num_rows, const int32_t* dst_row,
@@ -102,7 +102,7 @@ ep_status_t ep_get_device_error(const void* workspace, size_t workspace_bytes,
     const ep::WsHeader* hdr = static_cast<const ep::WsHeader*>(workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     int64_t v = 0;
-    if (hipMemcpyAsync(&v, &hdr->invalid_published, sizeof v, hipMemcpyDeviceToHost, s) !=
+    if (hipMemcpyAsync(&v, &hdr->num_invalid, sizeof v, hipMemcpyDeviceToHost, s) !=
         hipSuccess)
         return EP_ERR_HIP;
     if (hipStreamSynchronize(s) != hipSuccess) return EP_ERR_HIP;

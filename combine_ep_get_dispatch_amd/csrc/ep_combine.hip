@@ -14,7 +14,9 @@
 // 512-channel chunk), 8 channels per lane; lane k first fetches dst_row and
 // the weight of slot k, then every slot's 16-byte row segment is loaded
 // before the first FMA (K loads in flight per lane), and the result is
-// rounded with v_cvt_pk_bf16_f32 and written as one 16-byte store.  The slot
+// rounded with v_cvt_pk_bf16_f32 and written as one 16-byte store.  y and
+// out are streamed with the non-temporal hint (each byte is touched once), so
+// they do not displace the receive buffers that dispatch has just written.  The slot
 // count is a template parameter for the common top-k values so the loads
 // unroll; other K take a loop over groups of 8 slots.
 #include "ep_internal.h"
@@ -45,7 +47,7 @@ __device__ __forceinline__ void combine_slots(float (&acc)[8], const uint16_t* _
         const int d = __builtin_amdgcn_readlane(drow, k0 + i);
         v[i] = make_uint4(0, 0, 0, 0);
         if (k0 + i < kend && d >= 0 && act)
-            v[i] = *reinterpret_cast<const uint4*>(y + (int64_t)d * H + h0);
+            v[i] = load_nt(y + (int64_t)d * H + h0);
     }
 #pragma unroll
     for (int i = 0; i < KN; ++i) {
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
         o.y = pack_bf16x2(acc[2], acc[3]);
         o.z = pack_bf16x2(acc[4], acc[5]);
         o.w = pack_bf16x2(acc[6], acc[7]);
-        *reinterpret_cast<uint4*>(out + (int64_t)t * H + h0) = o;
+        store_nt(out + (int64_t)t * H + h0, o);
     }
 }
 

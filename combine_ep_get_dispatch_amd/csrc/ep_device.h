@@ -8,7 +8,30 @@
 namespace ep {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// 16-byte loads and stores with the non-temporal hint, for data that is
+// streamed exactly once (rows read once, outputs written once): they do not
+// displace reused data from the caches.
+__device__ __forceinline__ uint4 load_nt(const void* p) {
+    const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_nt(void* p, const uint4& v) {
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, static_cast<u32x4*>(p));
+}
+
+// 16-byte store with the device-scope cache policy (sc1): the line is
+// written through the XCD's L2 instead of staying dirty there.  Used for the
+// receive rows, which the next kernel reads from other XCDs: it leaves less
+// L2 write-back for the end of the kernel (measured faster than ordinary and
+// than non-temporal stores for dispatch's scattered rows).
+__device__ __forceinline__ void store_wt(void* p, const uint4& v) {
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(w) : "memory");
+}
 
 // bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 word.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

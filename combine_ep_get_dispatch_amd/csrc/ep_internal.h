@@ -15,33 +15,38 @@ constexpr int kLayoutThreads = 512;
 constexpr int kLayoutWaves = kLayoutThreads / 64;
 constexpr int kLayoutEntries = 2048;
 
+// Dynamic LDS the single-launch layout may use (gfx950 gives a workgroup up to
+// 160 KiB; a little is left for the kernel's static LDS).
+constexpr size_t kFusedLdsLimit = 156 * 1024;
+// ... and only for inputs of at most this many token blocks.
+constexpr int kFusedMaxBlocks = 2;
+
 __host__ __device__ inline int layout_tokens_per_block(int K) {
     int tb = kLayoutEntries / K;
     return tb < 1 ? 1 : tb;
 }
 
-// First 256 bytes of the caller's workspace.  `ticket`, `invalid_accum` are
-// zero between calls: the last layout workgroup resets them.
+// First 256 bytes of the caller's workspace, written by every layout call.
 struct WsHeader {
-    uint32_t ticket;            // workgroups of the current layout launch that finished
-    int32_t num_valid;          // N = valid slots of the last layout
-    int64_t invalid_accum;      // invalid slots counted by the running launch
-    int64_t invalid_published;  // invalid slots of the last completed layout
+    int32_t num_valid;     // N = valid slots of the last layout
+    int32_t pad;
+    int64_t num_invalid;   // invalid slots of the last layout
 };
 constexpr size_t kWsHeaderBytes = 256;
 static_assert(sizeof(WsHeader) <= kWsHeaderBytes, "header too large");
 
 // Workspace map for one shape (offsets in bytes from the workspace start):
-//   [0, 256)        WsHeader
-//   cnt  int32 [E][nb]   per-block expert counts, then (in place) per-block
-//                        bases: expert_offsets[e] + rows of e in earlier blocks
-//   pcnt int32 [P][nb]   per-block distinct-token counts per partition
-//   rank int32 [T*K]     rank of each slot among the earlier slots of its
-//                        expert inside its block (-1 if masked/invalid)
+//   [0, 256)           WsHeader
+//   cnt  int32 [nb][E] per-block expert counts
+//   pcnt int32 [nb][P] per-block distinct-token counts per partition
+//   inv  int32 [nb]    per-block invalid-slot counts
+//   rows int32 [T*K]   receive row of every slot (-1 if masked/invalid); the
+//                      count kernel leaves (expert << 12 | rank in block)
+//                      there and the finalize kernel turns it into the row
 struct WsMap {
     int nb = 0;        // token blocks
     int tb = 1;        // tokens per block
-    size_t cnt_off = 0, pcnt_off = 0, rank_off = 0, total = 0;
+    size_t cnt_off = 0, pcnt_off = 0, inv_off = 0, rows_off = 0, total = 0;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -52,23 +57,29 @@ inline WsMap ws_map(int T, int K, int E, int P) {
     m.nb = (T + m.tb - 1) / m.tb;
     m.cnt_off = kWsHeaderBytes;
     m.pcnt_off = m.cnt_off + align256(sizeof(int32_t) * (size_t)E * (size_t)m.nb);
-    m.rank_off = m.pcnt_off + align256(sizeof(int32_t) * (size_t)P * (size_t)m.nb);
-    m.total = m.rank_off + align256(sizeof(int32_t) * (size_t)T * (size_t)K);
+    m.inv_off = m.pcnt_off + align256(sizeof(int32_t) * (size_t)P * (size_t)m.nb);
+    m.rows_off = m.inv_off + align256(sizeof(int32_t) * (size_t)m.nb);
+    m.total = m.rows_off + align256(sizeof(int32_t) * (size_t)T * (size_t)K);
     return m;
 }
+
+// LDS the single-launch layout needs for this shape (it is used when this
+// fits in kFusedLdsLimit; larger inputs take the two-launch form).
+size_t layout_fused_lds_bytes(int T, int K, int E, int P);
 
 hipError_t launch_layout(const int64_t* idx, int T, int K, int E, int P, void* ws,
                          const WsMap& m, int32_t* cnt_e, int32_t* cnt_p, uint8_t* in_part,
                          int32_t* off_e, int32_t* off_p, hipStream_t s);
 
 // ---------------------------------------------------------------- dispatch --
-// One wave per (token, 1024-channel chunk); 16 channels per lane.
-constexpr int kDispatchThreads = 256;
+// One workgroup per token, one wave per 1024-channel chunk (16 channels per
+// lane), at most 16 waves; wider rows loop over their chunks.
+constexpr int kDispatchMaxThreads = 1024;
 constexpr int kDispatchChunk = 1024;
 
-hipError_t launch_dispatch(const uint16_t* x, int T, int H, const int64_t* idx, int K, int E,
-                           bool fp8, void* recv_x, float* recv_scales, int32_t* recv_src,
-                           int32_t* dst_row, const void* ws, const WsMap& m, hipStream_t s);
+hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K, bool fp8, void* recv_x,
+                           float* recv_scales, int32_t* recv_src, int32_t* dst_row,
+                           const void* ws, const WsMap& m, hipStream_t s);
 
 // ---------------------------------------------------------------- combine ---
 // One wave per (token, 512-channel chunk); 8 channels per lane.

@@ -62,10 +62,11 @@ typedef enum {
 
 /*
  * Bytes of device workspace that ep_get_dispatch_layout and ep_dispatch need
- * for this shape; 0 if the shape is invalid.  The first 256 bytes of a fresh
- * workspace must be zero (allocate it zero-filled once); every layout call
- * leaves them zero again, so the same workspace can serve any number of calls
- * and any shape up to its size.  One workspace serves one stream at a time.
+ * for this shape; 0 if the shape is invalid.  The workspace needs no
+ * initialisation: ep_get_dispatch_layout writes everything ep_dispatch and
+ * ep_get_device_error read from it.  A workspace may be reused for any shape
+ * it is large enough for; one workspace serves one layout -> dispatch
+ * sequence at a time.
  */
 size_t ep_workspace_bytes(int32_t num_tokens, int32_t num_topk, int32_t num_experts,
                           int32_t num_partitions);
@@ -83,9 +84,8 @@ size_t ep_workspace_bytes(int32_t num_tokens, int32_t num_topk, int32_t num_expe
  *   partition_offsets      [P+1]   expert_offsets[p * (E/P)]: partition p owns
  *                                  receive rows [partition_offsets[p],
  *                                  partition_offsets[p+1])
- * It also records, in the workspace, each slot's rank among the earlier slots
- * of the same expert (token-major, then slot order) and per-block bases, which
- * ep_dispatch turns into receive rows.  topk_idx is int64 [T*K].
+ * It also records, in the workspace, the receive row of every slot (see
+ * ep_dispatch), which ep_dispatch then uses.  topk_idx is int64 [T*K].
  * T may be 0 (all counts and offsets become 0).
  */
 ep_status_t ep_get_dispatch_layout(const int64_t *topk_idx, int32_t num_tokens,

@@ -46,11 +46,12 @@ def test_status_strings():
 
 def test_workspace_bytes():
     L = b.lib()
-    # header + cnt [E][nb] + pcnt [P][nb] + rank [T*K], each rounded up to 256 bytes
+    # header + cnt [nb][E] + pcnt [nb][P] + inv [nb] + rows [T*K], each rounded up
+    # to 256 bytes
     tb = 2048 // 8
     nb = -(-4096 // tb)
     r256 = lambda v: -(-v // 256) * 256
-    want = 256 + r256(4 * 256 * nb) + r256(4 * 64 * nb) + r256(4 * 4096 * 8)
+    want = 256 + r256(4 * 256 * nb) + r256(4 * 64 * nb) + r256(4 * nb) + r256(4 * 4096 * 8)
     assert L.ep_workspace_bytes(4096, 8, 256, 64) == want
     assert L.ep_workspace_bytes(0, 8, 256, 64) == 256
     for bad in [(-1, 2, 4, 2), (4, 0, 4, 2), (4, 2, 0, 1), (4, 2, 4, 0), (4, 2, 6, 4),

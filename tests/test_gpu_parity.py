@@ -44,6 +44,11 @@ GENERIC = [
     (50, 256, 1, 1, 1, 12, dict()),                          # a single expert
     (200, 640, 16, 1, 16, 13, dict(fp8=True)),               # P = 1 and K = E
     (100_000, 16, 4, 2, 1, 14, dict()),                      # many tokens, K = 1
+    # around the size where the layout switches from one launch (at most two
+    # blocks of 2048 slots) to two launches: 512 x 8 slots take one, 520 x 8 two
+    (512, 128, 256, 64, 8, 15, dict(masked_frac=0.02, invalid_frac=0.01)),
+    (520, 128, 256, 64, 8, 16, dict(masked_frac=0.02, invalid_frac=0.01)),
+    (9000, 128, 256, 64, 8, 17, dict(masked_frac=0.02, invalid_frac=0.01)),
 ]
 
 
