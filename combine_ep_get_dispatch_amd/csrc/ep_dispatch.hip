@@ -54,16 +54,18 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void dispatch_kernel(
         if (r >= hdr->num_valid) recv_src[r] = -1;
     }
 
-    for (int c = wave; c < nchunk; c += nw) {
-        const int h0 = c * kDispatchChunk + lane * 16;
-        const bool act0 = h0 < H;          // channels h0 .. h0+7
-        const bool act1 = h0 + 8 < H;      // channels h0+8 .. h0+15
-        const uint16_t* xs = x + (int64_t)t * H + h0;
-        uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-        if (act0) v0 = load_nt(xs);
-        if (act1) v1 = load_nt(xs + 8);
-
-        if constexpr (FP8) {
+    if constexpr (FP8) {
+        // Lane l quantises channels [16l, 16l + 16) of the chunk: its 128-channel
+        // group is lanes 8g .. 8g+7, and its 16 codes are one 16-byte store.
+        for (int c = wave; c < nchunk; c += nw) {
+            const int h0 = c * kDispatchChunk + lane * 16;
+            const bool act = h0 < H;       // H % 128 == 0: all 16 channels or none
+            const uint16_t* xs = x + (int64_t)t * H + h0;
+            uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
+            if (act) {
+                v0 = load_nt(xs);
+                v1 = load_nt(xs + 8);
+            }
             const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
             float f[16];
 #pragma unroll
@@ -83,19 +85,33 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void dispatch_kernel(
             q.y = e4m3x4_hw(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
             q.z = e4m3x4_hw(f[8] * inv, f[9] * inv, f[10] * inv, f[11] * inv);
             q.w = e4m3x4_hw(f[12] * inv, f[13] * inv, f[14] * inv, f[15] * inv);
-            if (act0 && (lane & 7) == 0) s_scale[h0 >> 7] = scale;
+            if (act && (lane & 7) == 0) s_scale[h0 >> 7] = scale;
             for (int k = 0; k < K; ++k) {
                 const int d = __builtin_amdgcn_readlane(drow, k);
                 if (d < 0) continue;
-                if (act0) store_wt(static_cast<uint8_t*>(recv_x) + (int64_t)d * H + h0, q);
+                if (act) store_wt(static_cast<uint8_t*>(recv_x) + (int64_t)d * H + h0, q);
             }
-        } else {
+        }
+    } else {
+        // Lane l copies channels [8l, 8l + 8) and [512 + 8l, 512 + 8l + 8) of
+        // the chunk, so every load and store instruction covers 1 KiB of
+        // consecutive bytes (whole cache lines).  Non-temporal stores measured
+        // fastest for these rows (bf16 receive rows are twice the FP8 bytes).
+        for (int c = wave; c < nchunk; c += nw) {
+            const int ha = c * kDispatchChunk + lane * 8;
+            const int hb = ha + kDispatchChunk / 2;
+            const bool act_a = ha < H;     // H % 8 == 0: all 8 channels or none
+            const bool act_b = hb < H;
+            const uint16_t* xs = x + (int64_t)t * H;
+            uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
+            if (act_a) va = *reinterpret_cast<const uint4*>(xs + ha);
+            if (act_b) vb = *reinterpret_cast<const uint4*>(xs + hb);
             for (int k = 0; k < K; ++k) {
                 const int d = __builtin_amdgcn_readlane(drow, k);
                 if (d < 0) continue;
-                uint16_t* dst = static_cast<uint16_t*>(recv_x) + (int64_t)d * H + h0;
-                if (act0) store_wt(dst, v0);
-                if (act1) store_wt(dst + 8, v1);
+                uint16_t* dst = static_cast<uint16_t*>(recv_x) + (int64_t)d * H;
+                if (act_a) store_nt(dst + ha, va);
+                if (act_b) store_nt(dst + hb, vb);
             }
         }
     }
