@@ -1,0 +1,84 @@
+"""The path captured in a HIP graph and replayed (GPU).
+
+Layout, dispatch and combine are captured once with preallocated outputs and
+replayed several times, with eager work and synchronisations between the
+replays; every replay must reproduce the eager results bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+from combine_ep_get_dispatch_amd import binding as ep
+from combine_ep_get_dispatch_amd import workloads as wl
+from parity import announce
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name,T", [("decode", None), ("prefill", 1024), ("coarse", 3000)])
+def test_graph_replays_match_eager(name, T):
+    case = wl.make(name, T=T)
+    announce("graph replay %s T=%d" % (name, case.T))
+    dev = torch.device("cuda:0")
+    idx = torch.from_numpy(case.topk_idx).to(dev)
+    x = torch.from_numpy(case.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.from_numpy(case.y_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    w = torch.from_numpy(case.topk_weights).to(dev)
+    T, K, E, P, H = case.T, case.K, case.E, case.P, case.H
+    R = T * K
+
+    def outputs():
+        lay = ep.Layout(torch.empty(E, dtype=torch.int32, device=dev),
+                        torch.empty(P, dtype=torch.int32, device=dev),
+                        torch.empty((T, P), dtype=torch.uint8, device=dev),
+                        torch.empty(E + 1, dtype=torch.int32, device=dev),
+                        torch.empty(P + 1, dtype=torch.int32, device=dev),
+                        ep.new_workspace(T, K, E, P, dev))
+        d = ep.Dispatched(
+            torch.empty((R, H), dtype=torch.uint8 if case.fp8 else torch.bfloat16, device=dev),
+            torch.empty((R, H // 128), dtype=torch.float32, device=dev) if case.fp8 else None,
+            torch.empty(R, dtype=torch.int32, device=dev),
+            torch.empty((T, K), dtype=torch.int32, device=dev))
+        return lay, d, torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def step(lay, d, out):
+        ep.get_dispatch_layout(idx, E, P, workspace=lay.workspace, out=lay)
+        ep.dispatch(x, idx, E, P, lay.workspace, fp8=case.fp8, out=d)
+        ep.combine(y, d.dst_row, w, out=out)
+
+    def snapshot(lay, d, out):
+        n = int(lay.expert_offsets[-1].item())
+        tensors = [lay.num_tokens_per_expert, lay.num_tokens_per_partition,
+                   lay.is_token_in_partition, lay.expert_offsets, lay.partition_offsets,
+                   d.recv_src_token, d.dst_row, d.recv_x[:n].view(torch.uint8),
+                   out.view(torch.int16)]
+        if case.fp8:
+            tensors.append(d.recv_scales[:n])
+        return [t.cpu().numpy().copy() for t in tensors]
+
+    ref = outputs()
+    step(*ref)
+    torch.cuda.synchronize()
+    want = snapshot(*ref)
+
+    bufs = outputs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(*bufs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(*bufs)
+    for rep in range(3):
+        # eager work between replays, and scribble over the outputs
+        bufs[2].fill_(0)
+        bufs[1].dst_row.fill_(-7)
+        step(*ref)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snapshot(*bufs)
+        for a, b in zip(got, want):
+            np.testing.assert_array_equal(a, b, err_msg="replay %d" % rep)
