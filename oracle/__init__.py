@@ -63,6 +63,10 @@ def _bind(lib):
     lib.oracle_quantize.argtypes = [_u16p, _i32, _i32, _u8p, _f32p]
     lib.oracle_dispatch_fp8.argtypes = [_u16p, _i32, _i32, _i32p, _i32, _u8p, _f32p]
     lib.oracle_combine.argtypes = [_u16p, _i32p, _f32p, _i32, _i32, _i32, _u16p]
+    lib.oracle_ll_layout.argtypes = [_i64p, _i32, _i32, _i32, _i32, _i32p, _i32p, _i32p]
+    lib.oracle_ll_layout.restype = _i64
+    lib.oracle_dispatch_rows_bf16.argtypes = [_u16p, _i32, _i32, _i32p, _i64, _u16p]
+    lib.oracle_dispatch_rows_fp8.argtypes = [_u16p, _i32, _i32, _i32p, _i64, _u8p, _f32p]
     return lib
 
 
@@ -204,6 +208,60 @@ def combine(y_bits: np.ndarray, dst_row: np.ndarray, topk_weights: np.ndarray) -
     _load().oracle_combine(_ptr(y, ctypes.c_uint16), _ptr(dst, ctypes.c_int32),
                            _ptr(w, ctypes.c_float), T, K, H, _ptr(out, ctypes.c_uint16))
     return out
+
+
+def ll_layout(topk_idx: np.ndarray, E: int, C: int) -> dict:
+    """Fixed-capacity layout (see ``oracle_ll_layout``): expert e owns rows
+    [e*C, (e+1)*C)."""
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
+    T, K = idx.shape
+    cnt_e = np.empty(E, np.int32)
+    dst = np.empty((T, K), np.int32)
+    src = np.empty(E * C, np.int32)
+    nerr = _load().oracle_ll_layout(_ptr(idx, ctypes.c_int64), T, K, E, C,
+                                    _ptr(cnt_e, ctypes.c_int32), _ptr(dst, ctypes.c_int32),
+                                    _ptr(src, ctypes.c_int32))
+    return dict(num_tokens_per_expert=cnt_e, dst_row=dst, recv_src_token=src,
+                num_invalid=int(nerr))
+
+
+def dispatch_rows_bf16(x_bits: np.ndarray, recv_src_token: np.ndarray, fill: int = 0):
+    """bf16 rows [R, H] for a source map with -1 holes; holes hold ``fill``."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    T, H = x.shape
+    src = np.ascontiguousarray(recv_src_token, dtype=np.int32)
+    out = np.full((src.size, H), fill, np.uint16)
+    _load().oracle_dispatch_rows_bf16(_ptr(x, ctypes.c_uint16), T, H, _ptr(src, ctypes.c_int32),
+                                      src.size, _ptr(out, ctypes.c_uint16))
+    return out
+
+
+def dispatch_rows_fp8(x_bits: np.ndarray, recv_src_token: np.ndarray, fill: int = 0):
+    """FP8 rows [R, H] uint8 and scales [R, H/128] for a source map with -1
+    holes; hole bytes hold ``fill`` and hole scales 0."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    T, H = x.shape
+    assert H % 128 == 0
+    src = np.ascontiguousarray(recv_src_token, dtype=np.int32)
+    rx = np.full((src.size, H), fill, np.uint8)
+    rs = np.zeros((src.size, H // 128), np.float32)
+    _load().oracle_dispatch_rows_fp8(_ptr(x, ctypes.c_uint16), T, H, _ptr(src, ctypes.c_int32),
+                                     src.size, _ptr(rx, ctypes.c_uint8), _ptr(rs, ctypes.c_float))
+    return rx, rs
+
+
+def run_ll(topk_idx, x_bits, E, C, fp8, y_bits=None, topk_weights=None) -> dict:
+    """The decode path: fixed-capacity layout, dispatch and (optionally)
+    combine of expert outputs y [E*C, H] laid out like the receive rows."""
+    res = ll_layout(topk_idx, E, C)
+    src = res["recv_src_token"]
+    if fp8:
+        res["recv_x"], res["recv_scales"] = dispatch_rows_fp8(x_bits, src)
+    else:
+        res["recv_x"] = dispatch_rows_bf16(x_bits, src)
+    if y_bits is not None:
+        res["out"] = combine(y_bits, res["dst_row"], topk_weights)
+    return res
 
 
 def run(topk_idx, x_bits, E, P, fp8, y_bits=None, topk_weights=None) -> dict:

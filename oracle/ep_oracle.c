@@ -310,6 +310,95 @@ void oracle_dispatch_fp8(const uint16_t *x, int32_t T, int32_t H,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Fixed-capacity receive layout (decode variant)                            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Besides the throughput kernels, the library has a second family for
+ * inference decoding: small batches, lowest latency ("DeepSeek releases
+ * DeepEP ...", section "Technical Details"; the 128-token, top-8 decode case
+ * is in "Deepseek Ai Deepep: A library for an open-open EP for example
+ * training", section "Technological Views and Benefits").  The pages give no
+ * buffer layout for it.  This oracle takes a fixed-capacity one, in which no
+ * row number depends on the counts of other experts:
+ *   expert e owns receive rows [e*C, (e+1)*C), C = capacity per expert
+ *   a valid slot (t,k) of expert e whose rank among expert e's valid slots,
+ *   in (token, slot) order, is r gets row e*C + r when r < C; when r >= C it
+ *   is dropped (dst = -1)
+ *   cnt_e [E]    valid slots routed to expert e (dropped ones included)
+ *   dst   [T][K] receive row of slot (t,k), or -1 (masked, invalid, dropped)
+ *   src   [E*C]  source token of each receive row, -1 where no slot landed
+ * Returns the number of invalid slots (outside [0, E) and not -1).
+ */
+int64_t oracle_ll_layout(const int64_t *idx, int32_t T, int32_t K, int32_t E, int32_t C,
+                         int32_t *cnt_e, int32_t *dst, int32_t *src)
+{
+    int64_t nerr = 0;
+    for (int32_t e = 0; e < E; ++e)
+        cnt_e[e] = 0;
+    for (int64_t r = 0; r < (int64_t)E * C; ++r)
+        src[r] = -1;
+    for (int32_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int64_t v = idx[(int64_t)t * K + k];
+            int32_t row = -1;
+            if (v >= 0 && v < E) {
+                int32_t rank = cnt_e[v];
+                cnt_e[v] += 1;
+                if (rank < C) {
+                    row = (int32_t)v * C + rank;
+                    src[row] = t;
+                }
+            } else if (v != -1) {
+                nerr += 1;
+            }
+            dst[(int64_t)t * K + k] = row;
+        }
+    }
+    return nerr;
+}
+
+/*
+ * Dispatch into receive rows named by a source-token map: each row r in
+ * [0, R) with src[r] >= 0 becomes token src[r]'s row (bf16 bits, or FP8
+ * codes and scales from oracle_quantize); rows with src[r] = -1 are left
+ * unwritten.
+ */
+void oracle_dispatch_rows_bf16(const uint16_t *x, int32_t T, int32_t H,
+                               const int32_t *src, int64_t R, uint16_t *recv_x)
+{
+    (void)T;
+    for (int64_t r = 0; r < R; ++r) {
+        int64_t t = src[r];
+        if (t < 0)
+            continue;
+        for (int64_t h = 0; h < H; ++h)
+            recv_x[r * H + h] = x[t * H + h];
+    }
+}
+
+void oracle_dispatch_rows_fp8(const uint16_t *x, int32_t T, int32_t H,
+                              const int32_t *src, int64_t R,
+                              uint8_t *recv_x, float *recv_scales)
+{
+    int32_t G = H / 128;
+    uint8_t *q = (uint8_t *)malloc((size_t)T * (size_t)H + 1);
+    float *s = (float *)malloc(((size_t)T * (size_t)G + 1) * sizeof(float));
+    oracle_quantize(x, T, H, q, s);
+    for (int64_t r = 0; r < R; ++r) {
+        int64_t t = src[r];
+        if (t < 0)
+            continue;
+        for (int64_t h = 0; h < H; ++h)
+            recv_x[r * H + h] = q[t * H + h];
+        for (int32_t g = 0; g < G; ++g)
+            recv_scales[r * G + g] = s[t * G + g];
+    }
+    free(q);
+    free(s);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Combine                                                                   */
 /* ------------------------------------------------------------------------ */
 

@@ -186,3 +186,36 @@ def layout_batch(idx_batch: np.ndarray, E: int, P: int):
     nerr = (~valid & (flat != -1)).sum(axis=1)
     return cnt_e, in_part.astype(np.uint8), off_e.astype(np.int32), \
         dst.reshape(B, T, K).astype(np.int32), nerr
+
+
+def ll_layout(idx: np.ndarray, E: int, C: int) -> dict:
+    """Fixed-capacity layout from the stable-sort permutation above: a slot's
+    rank inside its expert is its sorted position minus the expert's start."""
+    idx = np.asarray(idx, np.int64)
+    T, K = idx.shape
+    lay = layout(idx, E, 1)
+    dst, _ = permutation(idx, E)
+    flat = idx.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    e_safe = np.where(valid, flat, 0)
+    rank = dst.reshape(-1) - lay["expert_offsets"][e_safe]
+    keep = valid & (rank < C)
+    ll = np.where(keep, e_safe * C + rank, -1).astype(np.int32)
+    src = np.full(E * C, -1, np.int32)
+    src[ll[keep]] = np.nonzero(keep)[0] // K
+    return dict(num_tokens_per_expert=lay["num_tokens_per_expert"], dst_row=ll.reshape(T, K),
+                recv_src_token=src, num_invalid=lay["num_invalid"])
+
+
+def ll_rank_batch(idx_batch: np.ndarray, E: int) -> np.ndarray:
+    """Rank of each slot among the earlier valid slots of the same expert, by
+    direct pairwise comparison over a batch of small [T,K] tensors; -1 for
+    slots that are not valid."""
+    B, T, K = idx_batch.shape
+    flat = idx_batch.reshape(B, T * K)
+    valid = (flat >= 0) & (flat < E)
+    n = T * K
+    earlier = np.tril(np.ones((n, n), bool), k=-1)
+    same = (flat[:, :, None] == flat[:, None, :]) & valid[:, None, :]
+    rank = (same & earlier[None]).sum(axis=2)
+    return np.where(valid, rank, -1).reshape(B, T, K)

@@ -33,6 +33,11 @@ COMBINE = [lambda: pins.test_combine_hand_worked(GOLDEN), pins.test_combine_exac
            pins.test_combine_rounding_sensitive_cases]
 DISPATCH = [pins.test_bf16_dispatch_rows_are_bitwise_copies,
             pins.test_fp8_dispatch_rows_are_quantised_tokens]
+LL = [lambda: pins.test_ll_layout_hand_worked(GOLDEN),
+      lambda: pins.test_ll_layout_random_against_library_routines(1),
+      lambda: pins.test_ll_layout_random_against_library_routines(4),
+      pins.test_ll_layout_matches_offsets_layout_when_nothing_drops,
+      pins.test_ll_dispatch_rows_are_copies_and_holes_untouched]
 
 PERM_LOOP = """    for (int32_t t = 0; t < T; ++t) {
         for (int32_t k = 0; k < K; ++k) {
@@ -86,11 +91,22 @@ MUTANTS = [
      "{ uint32_t u_; memcpy(&u_, &acc, 4); out[t * H + h] = (uint16_t)(u_ >> 16); }", COMBINE),
     ("combine weight of the wrong slot", "acc = fmaf(w[t * K + k],",
      "acc = fmaf(w[t * K + (K - 1 - k)],", COMBINE),
+    ("ll capacity off by one", "if (rank < C) {", "if (rank <= C) {", LL),
+    ("ll rows strided by top-k", "row = (int32_t)v * C + rank;",
+     "row = (int32_t)v * K + rank;", LL),
+    ("ll count stops at capacity", "                cnt_e[v] += 1;\n                if (rank < C) {",
+     "                if (rank < C) {\n                    cnt_e[v] += 1;", LL),
+    ("ll holes not marked", "    for (int64_t r = 0; r < (int64_t)E * C; ++r)\n        src[r] = -1;\n", "", LL),
+    ("ll dispatch fills holes",
+     "if (t < 0)\n            continue;\n        for (int64_t h = 0; h < H; ++h)\n"
+     "            recv_x[r * H + h] = x[t * H + h];",
+     "if (t < 0)\n            t = 0;\n        for (int64_t h = 0; h < H; ++h)\n"
+     "            recv_x[r * H + h] = x[t * H + h];", LL),
 ]
 
 
 GROUPS = {"E4M3": E4M3, "BF16": BF16, "LAYOUT": LAYOUT, "QUANT": QUANT,
-          "COMBINE": COMBINE, "DISPATCH": DISPATCH}
+          "COMBINE": COMBINE, "DISPATCH": DISPATCH, "LL": LL}
 
 
 def _group_name(checks):

@@ -224,6 +224,109 @@ def test_layout_of_each_configuration(name):
 
 
 # ---------------------------------------------------------------------------
+# fixed-capacity (decode) layout
+# ---------------------------------------------------------------------------
+
+def test_ll_layout_hand_worked(golden_dir):
+    g = _read_kv(os.path.join(golden_dir, "ll_layout_hand_worked.txt"))
+    T, K, E = (int(g[k][0]) for k in "TKE")
+    idx = np.array(g["topk_idx"], np.int64).reshape(T, K)
+    for C in (1, 2):
+        got = oracle.ll_layout(idx, E, C)
+        np.testing.assert_array_equal(got["num_tokens_per_expert"],
+                                      np.array(g["num_tokens_per_expert"], np.int32))
+        np.testing.assert_array_equal(got["dst_row"].reshape(-1),
+                                      np.array(g["C%d_dst_row" % C], np.int32))
+        np.testing.assert_array_equal(got["recv_src_token"],
+                                      np.array(g["C%d_recv_src_token" % C], np.int32))
+        assert got["num_invalid"] == 0
+
+
+@pytest.mark.parametrize("T,K", [(1, 5), (2, 2), (3, 2), (5, 1), (1, 1)])
+def test_ll_layout_exhaustive_small(T, K):
+    """Every routing tensor of this shape with ids in {-1, 0, 1, 2} (masked
+    slots and repeated experts included), E = 3, capacities 1..3, against
+    ranks from direct pairwise comparison."""
+    E = 3
+    n = T * K
+    grid = np.array(np.meshgrid(*[np.arange(-1, E)] * n, indexing="ij")).reshape(n, -1).T
+    batch = grid.reshape(-1, T, K).astype(np.int64)
+    rank = bf.ll_rank_batch(batch, E)
+    for C in (1, 2, 3):
+        want_dst = np.where((rank >= 0) & (rank < C), batch * C + rank, -1)
+        for i in range(batch.shape[0]):
+            got = oracle.ll_layout(batch[i], E, C)
+            assert np.array_equal(got["dst_row"], want_dst[i]), (batch[i], C)
+            cnt = np.bincount(batch[i][batch[i] >= 0], minlength=E)
+            assert np.array_equal(got["num_tokens_per_expert"], cnt)
+            src = np.full(E * C, -1, np.int32)
+            for t in range(T):
+                for k in range(K):
+                    if want_dst[i, t, k] >= 0:
+                        src[want_dst[i, t, k]] = t
+            assert np.array_equal(got["recv_src_token"], src)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_ll_layout_random_against_library_routines(seed):
+    rng = np.random.default_rng(1000 + seed)
+    E = int(rng.choice([1, 2, 4, 8, 16, 32, 64, 256]))
+    K = int(rng.integers(1, min(E, 8) + 1))
+    T = int(rng.integers(0, 300))
+    c = wl.random_case(T, 8, E, 1, K, seed, masked_frac=0.1 * (seed % 3),
+                       invalid_frac=0.05 * (seed % 2), allow_dup=bool(seed % 2),
+                       skew=float(seed % 4), with_y=False)
+    cnt = np.bincount(c.topk_idx[(c.topk_idx >= 0) & (c.topk_idx < E)], minlength=E)
+    for C in {1, max(1, int(cnt.max(initial=0)) // 2), max(1, int(cnt.max(initial=0))), T + 1}:
+        got = oracle.ll_layout(c.topk_idx, E, C)
+        want = bf.ll_layout(c.topk_idx, E, C)
+        for k in want:
+            np.testing.assert_array_equal(np.asarray(got[k]), np.asarray(want[k]), err_msg=k)
+        # invariants: expert e's kept slots fill rows e*C .. e*C + min(cnt, C) - 1
+        dst = got["dst_row"]
+        kept = dst >= 0
+        assert int(kept.sum()) == int(np.minimum(cnt, C).sum())
+        filled = got["recv_src_token"].reshape(E, C) >= 0
+        assert np.array_equal(filled.sum(axis=1), np.minimum(cnt, C))
+        assert np.all(filled == (np.arange(C)[None, :] < np.minimum(cnt, C)[:, None]))
+        assert np.all(dst[kept] // C == c.topk_idx[kept])
+
+
+def test_ll_layout_matches_offsets_layout_when_nothing_drops():
+    """With capacity >= every expert's count, a slot's row inside its expert
+    is the same in both layouts."""
+    c = wl.random_case(257, 8, 64, 8, 6, 21, masked_frac=0.1, invalid_frac=0.02,
+                       allow_dup=True, skew=2.0, with_y=False)
+    lay = oracle.layout(c.topk_idx, 64, 8)
+    dst, _ = oracle.permutation(c.topk_idx, 64, lay["expert_offsets"])
+    C = int(lay["num_tokens_per_expert"].max())
+    ll = oracle.ll_layout(c.topk_idx, 64, C)
+    assert ll["num_invalid"] == lay["num_invalid"] > 0
+    np.testing.assert_array_equal(ll["num_tokens_per_expert"], lay["num_tokens_per_expert"])
+    valid = dst >= 0
+    e = c.topk_idx[valid]
+    np.testing.assert_array_equal(ll["dst_row"][valid] - e * C,
+                                  dst[valid] - lay["expert_offsets"][e])
+    assert np.all(ll["dst_row"][~valid] == -1)
+
+
+def test_ll_dispatch_rows_are_copies_and_holes_untouched():
+    c = wl.random_case(60, 256, 16, 4, 4, 23, masked_frac=0.1, allow_dup=True)
+    res_b = oracle.run_ll(c.topk_idx, c.x_bits, 16, 16, fp8=False)
+    src = res_b["recv_src_token"]
+    rx = oracle.dispatch_rows_bf16(c.x_bits, src, fill=0xABCD)
+    rq, rs = oracle.dispatch_rows_fp8(c.x_bits, src, fill=0x5A)
+    q, s = oracle.quantize(c.x_bits)
+    hole = src < 0
+    assert hole.any() and (~hole).any()
+    assert np.all(rx[hole] == 0xABCD) and np.all(rq[hole] == 0x5A) and np.all(rs[hole] == 0)
+    np.testing.assert_array_equal(rx[~hole], c.x_bits[src[~hole]])
+    np.testing.assert_array_equal(rq[~hole], q[src[~hole]])
+    np.testing.assert_array_equal(rs[~hole], s[src[~hole]])
+    np.testing.assert_array_equal(res_b["recv_x"][~hole], rx[~hole])
+
+
+# ---------------------------------------------------------------------------
 # FP8 quantiser
 # ---------------------------------------------------------------------------
 
