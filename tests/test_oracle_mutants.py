@@ -50,6 +50,17 @@ PERM_LOOP_SLOT_MAJOR = """    for (int32_t k = 0; k < K; ++k) {
             if (v >= 0 && v < E) {
                 int32_t r"""
 
+# The row copies of the offsets-layout dispatch (the fixed-capacity dispatch
+# has a hole test between these lines, so the anchors stay unique).
+BF16_ROW_COPY = """        int64_t t = src[r];
+        for (int64_t h = 0; h < H; ++h)
+            recv_x[r * H + h] = x[t * H + h];"""
+FP8_ROW_COPY = """        int64_t t = src[r];
+        for (int64_t h = 0; h < H; ++h)
+            recv_x[r * H + h] = q[t * H + h];
+        for (int32_t g = 0; g < G; ++g)
+            recv_scales[r * G + g] = s[t * G + g];"""
+
 MUTANTS = [
     ("e4m3 ties away from zero", "double q = nearbyint(a / ldexp(1.0, E - 3));",
      "double q = round(a / ldexp(1.0, E - 3));", E4M3),
@@ -77,10 +88,10 @@ MUTANTS = [
     ("amax floor dropped", "float ac = (a > 1e-4f) ? a : 1e-4f;", "float ac = a;", QUANT),
     ("amax without abs", "float v = fabsf(bf16_to_f32(x[t * H + 128 * g + j]));",
      "float v = bf16_to_f32(x[t * H + 128 * g + j]);", QUANT),
-    ("fp8 dispatch copies the wrong scale", "recv_scales[r * G + g] = s[t * G + g];",
-     "recv_scales[r * G + g] = s[r % 1 * G + g];", DISPATCH),
-    ("bf16 dispatch copies by row index", "recv_x[r * H + h] = x[t * H + h];",
-     "recv_x[r * H + h] = x[(r % T) * H + h];", DISPATCH),
+    ("fp8 dispatch copies the wrong scale", FP8_ROW_COPY,
+     FP8_ROW_COPY.replace("= s[t * G + g];", "= s[r % 1 * G + g];"), DISPATCH),
+    ("bf16 dispatch copies by row index", BF16_ROW_COPY,
+     BF16_ROW_COPY.replace("= x[t * H + h];", "= x[(r % T) * H + h];"), DISPATCH),
     ("combine ignores weights", "acc = fmaf(w[t * K + k], bf16_to_f32(y[r * H + h]), acc);",
      "acc = acc + bf16_to_f32(y[r * H + h]);", COMBINE),
     ("combine unfused", "acc = fmaf(w[t * K + k], bf16_to_f32(y[r * H + h]), acc);",
