@@ -23,6 +23,7 @@ EP_DTYPE_BF16 = 0
 EP_DTYPE_FP8_E4M3 = 1
 MAX_EXPERTS = 1024
 MAX_TOPK = 64
+LL_MAX_SLOTS = 8192
 
 
 class EpError(RuntimeError):
@@ -44,6 +45,8 @@ SIGNATURES = {
     "ep_dispatch": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _i32, ctypes.c_int, _vp,
                                    _vp, _vp, _vp, _vp, _sz, _vp]),
     "ep_combine": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "ep_low_latency_dispatch": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _i32,
+                                               ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ep_get_device_error": (ctypes.c_int, [_vp, _sz, ctypes.POINTER(_i64), _vp]),
     "ep_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ep_convert_e4m3": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp]),
@@ -205,6 +208,53 @@ def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_part
         EP_DTYPE_FP8_E4M3 if fp8 else EP_DTYPE_BF16, _ptr(out.recv_x),
         _ptr(out.recv_scales) if fp8 else None, _ptr(out.recv_src_token), _ptr(out.dst_row),
         _ptr(workspace), workspace.numel(), _stream(x)), "ep_dispatch")
+    return out
+
+
+@dataclass
+class LowLatencyDispatched:
+    num_tokens_per_expert: torch.Tensor  # [E] int32 (dropped slots included)
+    recv_x: torch.Tensor                 # [E*C, H] bf16, or uint8 E4M3 codes
+    recv_scales: torch.Tensor | None     # [E*C, H/128] float32 (FP8 only)
+    recv_src_token: torch.Tensor         # [E*C] int32, -1 for unfilled rows
+    dst_row: torch.Tensor                # [T, K] int32
+    num_invalid: torch.Tensor            # [1] int64
+
+
+def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int,
+                         capacity: int, fp8: bool = False,
+                         out: LowLatencyDispatched | None = None) -> LowLatencyDispatched:
+    """ep_low_latency_dispatch: x [T, H] bf16 -> fixed-capacity rows, expert
+    e owning rows [e*C, (e+1)*C), in one launch."""
+    if x.dim() != 2 or topk_idx.dim() != 2:
+        raise ValueError("x must be [T, H] and topk_idx [T, K]")
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    E, C = int(num_experts), int(capacity)
+    _need(x, torch.bfloat16, "x")
+    _need(topk_idx, torch.int64, "topk_idx", (T, K))
+    dev = x.device
+    R = E * C
+    if out is None:
+        out = LowLatencyDispatched(
+            torch.empty(E, dtype=torch.int32, device=dev),
+            torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev),
+            torch.empty((R, H // 128), dtype=torch.float32, device=dev) if fp8 else None,
+            torch.empty(R, dtype=torch.int32, device=dev),
+            torch.empty((T, K), dtype=torch.int32, device=dev),
+            torch.empty(1, dtype=torch.int64, device=dev))
+    _need(out.num_tokens_per_expert, torch.int32, "num_tokens_per_expert", (E,))
+    _need(out.recv_x, torch.uint8 if fp8 else torch.bfloat16, "recv_x", (R, H))
+    if fp8:
+        _need(out.recv_scales, torch.float32, "recv_scales", (R, H // 128))
+    _need(out.recv_src_token, torch.int32, "recv_src_token", (R,))
+    _need(out.dst_row, torch.int32, "dst_row", (T, K))
+    _need(out.num_invalid, torch.int64, "num_invalid", (1,))
+    _check(lib().ep_low_latency_dispatch(
+        _ptr(x), T, H, _ptr(topk_idx), K, E, C, EP_DTYPE_FP8_E4M3 if fp8 else EP_DTYPE_BF16,
+        _ptr(out.num_tokens_per_expert), _ptr(out.recv_x),
+        _ptr(out.recv_scales) if fp8 else None, _ptr(out.recv_src_token), _ptr(out.dst_row),
+        _ptr(out.num_invalid), _stream(x)), "ep_low_latency_dispatch")
     return out
 
 

@@ -78,6 +78,32 @@ ep_status_t ep_dispatch(const void* x, int32_t num_tokens, int32_t hidden,
                                         static_cast<hipStream_t>(stream)));
 }
 
+ep_status_t ep_low_latency_dispatch(const void* x, int32_t num_tokens, int32_t hidden,
+                                    const int64_t* topk_idx, int32_t num_topk,
+                                    int32_t num_experts, int32_t capacity, ep_dtype_t out_dtype,
+                                    int32_t* num_tokens_per_expert, void* recv_x,
+                                    float* recv_scales, int32_t* recv_src_token,
+                                    int32_t* dst_row, int64_t* num_invalid, void* stream) {
+    const int32_t T = num_tokens, H = hidden, K = num_topk, E = num_experts, C = capacity;
+    ep_status_t st = check_routing_shape(T, K, E, 1);
+    if (st != EP_OK) return st;
+    if (C <= 0 || (int64_t)E * C >= kMaxRows) return EP_ERR_INVALID_ARG;
+    if (out_dtype != EP_DTYPE_BF16 && out_dtype != EP_DTYPE_FP8_E4M3) return EP_ERR_INVALID_ARG;
+    const bool fp8 = out_dtype == EP_DTYPE_FP8_E4M3;
+    if (H <= 0 || H % 8 != 0 || (fp8 && H % 128 != 0)) return EP_ERR_INVALID_ARG;
+    if (!num_tokens_per_expert || !recv_src_token) return EP_ERR_INVALID_ARG;
+    if (T > 0) {
+        if (!x || !topk_idx || !recv_x || !dst_row) return EP_ERR_INVALID_ARG;
+        if (fp8 && !recv_scales) return EP_ERR_INVALID_ARG;
+        if (!aligned16(x) || !aligned16(recv_x)) return EP_ERR_INVALID_ARG;
+    }
+    if ((int64_t)T * K > EP_LL_MAX_SLOTS) return EP_ERR_UNSUPPORTED;
+    return from_hip(ep::launch_ll_dispatch(
+        static_cast<const uint16_t*>(x), topk_idx, T, H, K, E, C, fp8, num_tokens_per_expert,
+        recv_x, recv_scales, recv_src_token, dst_row, num_invalid,
+        static_cast<hipStream_t>(stream)));
+}
+
 ep_status_t ep_combine(const void* y, int64_t num_rows, const int32_t* dst_row,
                        const float* topk_weights, int32_t num_tokens, int32_t num_topk,
                        int32_t hidden, void* out, void* stream) {

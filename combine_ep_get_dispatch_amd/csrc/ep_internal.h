@@ -81,6 +81,19 @@ hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K, bool fp8, voi
                            float* recv_scales, int32_t* recv_src, int32_t* dst_row,
                            const void* ws, const WsMap& m, hipStream_t s);
 
+// Fixed-capacity (decode) dispatch: one launch, one workgroup per token (one
+// workgroup when T = 0), at least kLlMinWaves waves so the routing scan that
+// every workgroup does has threads enough.  LDS: two [E] int histograms and,
+// for FP8, the token's G scales.
+constexpr int kLlMinWaves = 4;
+
+size_t ll_dispatch_lds_bytes(int E, int H, bool fp8);
+
+hipError_t launch_ll_dispatch(const uint16_t* x, const int64_t* idx, int T, int H, int K, int E,
+                              int C, bool fp8, int32_t* cnt_e, void* recv_x, float* recv_scales,
+                              int32_t* recv_src, int32_t* dst_row, int64_t* num_invalid,
+                              hipStream_t s);
+
 // ---------------------------------------------------------------- combine ---
 // One wave per (token, 512-channel chunk); 8 channels per lane; two waves per
 // workgroup (measured ~3% faster than 4 or 8 and slightly faster than 1).

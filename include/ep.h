@@ -59,6 +59,7 @@ typedef enum {
 /* Limits of this build (EP_ERR_UNSUPPORTED beyond them). */
 #define EP_MAX_EXPERTS 1024
 #define EP_MAX_TOPK 64
+#define EP_LL_MAX_SLOTS 8192   /* T*K of one ep_low_latency_dispatch call */
 
 /*
  * Bytes of device workspace that ep_get_dispatch_layout and ep_dispatch need
@@ -146,6 +147,49 @@ ep_status_t ep_dispatch(const void *x, int32_t num_tokens, int32_t hidden,
 ep_status_t ep_combine(const void *y, int64_t num_rows, const int32_t *dst_row,
                        const float *topk_weights, int32_t num_tokens, int32_t num_topk,
                        int32_t hidden, void *out, void *stream);
+
+/*
+ * Decode dispatch into fixed-capacity receive buffers, in a single kernel
+ * launch.  Besides its throughput kernels the library family serves
+ * inference decoding with kernels built for small batches and the lowest
+ * latency ("DeepSeek releases DeepEP, an efficient communication library for
+ * MoE models", section "Technical Details"; the 128-token, top-8 decode case
+ * is in "Deepseek Ai Deepep: A library for an open-open EP for example
+ * training", section "Technological Views and Benefits").  The pages give no
+ * buffer layout for it; this library's is a fixed capacity C per expert, so
+ * no receive row depends on a prefix sum over the experts and nothing has to
+ * wait for one:
+ *   expert e owns receive rows [e*C, (e+1)*C) (partition p, holding experts
+ *   [p*E/P, (p+1)*E/P), owns the contiguous rows [p*(E/P)*C, (p+1)*(E/P)*C));
+ *   a valid slot (t,k) of expert e whose rank among expert e's valid slots,
+ *   in token-major then slot order, is r gets
+ *     dst_row[t*K+k] = e*C + r   if r < C,
+ *   and is dropped (dst_row = -1) if r >= C; masked and invalid slots get -1.
+ *   num_tokens_per_expert [E] counts all valid slots of e, dropped ones
+ *   included, so rows e*C .. e*C + min(count, C) - 1 are filled and
+ *   count > C reports drops (C >= T can drop nothing unless a token repeats
+ *   an expert).
+ *   recv_src_token [E*C]: the source token of each filled row, -1 elsewhere.
+ *   recv_x [E*C*H] (bf16, or uint8 E4M3 codes) and recv_scales [E*C*G] hold
+ *   the filled rows exactly as ep_dispatch writes them (same copy and same
+ *   quantiser); unfilled rows are left untouched.
+ *   num_invalid: device pointer to one int64 that receives the number of
+ *   invalid topk_idx entries (not -1 and outside [0, E)), or NULL.
+ * ep_combine runs on the result unchanged, with y [E*C, H] laid out like the
+ * receive rows and num_rows = E*C.  Every output is written by this one
+ * launch; no workspace, no initialisation, no host synchronisation.
+ * x bf16 [T*H], topk_idx int64 [T*K]; H % 8 == 0 (H % 128 == 0 for FP8);
+ * capacity >= 1; E*C < 2^31.  T may be 0 (counts 0, every row -1).
+ * EP_ERR_UNSUPPORTED when T*K > EP_LL_MAX_SLOTS (every workgroup reads the
+ * whole routing tensor: use ep_get_dispatch_layout + ep_dispatch for large
+ * batches), E > EP_MAX_EXPERTS or K > EP_MAX_TOPK.
+ */
+ep_status_t ep_low_latency_dispatch(const void *x, int32_t num_tokens, int32_t hidden,
+                                    const int64_t *topk_idx, int32_t num_topk,
+                                    int32_t num_experts, int32_t capacity,
+                                    ep_dtype_t out_dtype, int32_t *num_tokens_per_expert,
+                                    void *recv_x, float *recv_scales, int32_t *recv_src_token,
+                                    int32_t *dst_row, int64_t *num_invalid, void *stream);
 
 /*
  * Waits for `stream`, then stores in *num_invalid the number of invalid

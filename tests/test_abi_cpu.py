@@ -126,6 +126,29 @@ def test_dispatch_rejects_bad_arguments(buf):
     assert call(wsz=128) == WORKSPACE
 
 
+def test_low_latency_dispatch_rejects_bad_arguments(buf):
+    L = b.lib()
+    x, idx, cnt, rx, rs, src, dst = (buf() for _ in range(7))
+
+    def call(x=x, T=4, H=256, idx=idx, K=2, E=4, C=4, dt=0, cnt=cnt, rx=rx, rs=rs, src=src,
+             dst=dst, inv=None):
+        return L.ep_low_latency_dispatch(x, T, H, idx, K, E, C, dt, cnt, rx, rs, src, dst, inv,
+                                         None)
+
+    for kw in [dict(x=None), dict(idx=None), dict(cnt=None), dict(rx=None), dict(src=None),
+               dict(dst=None), dict(H=0), dict(H=12), dict(dt=2), dict(dt=1, H=136),
+               dict(dt=1, rs=None), dict(K=5), dict(K=0), dict(E=0), dict(T=-3), dict(C=0),
+               dict(C=-1), dict(E=1024, C=1 << 21),
+               dict(x=ctypes.c_void_p(0x100008)), dict(rx=ctypes.c_void_p(0x100004))]:
+        assert call(**kw) == INVALID, kw
+    # T = 0 needs no token buffers, but the counts and the row map still
+    assert call(T=0, cnt=None) == INVALID and call(T=0, src=None) == INVALID
+    assert call(E=2048) == UNSUPPORTED
+    assert call(K=65, E=128) == UNSUPPORTED
+    assert call(T=1025, K=8, E=16) == UNSUPPORTED     # T*K > EP_LL_MAX_SLOTS
+    assert b.LL_MAX_SLOTS == 8192
+
+
 def test_combine_rejects_bad_arguments(buf):
     L = b.lib()
     y, dst, w, out = (buf() for _ in range(4))
