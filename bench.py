@@ -9,6 +9,12 @@ bf16 weighted combine).
 
     python bench.py [--steps K] [--warmup W] [--config prefill|decode|...]
 
+    python bench.py --low-latency [--config decode] [--capacity C]
+
+`--low-latency` times the decode path instead: ep_low_latency_dispatch (one
+launch, fixed capacity C per expert, default C = T) -> ep_combine on expert
+outputs laid out like its receive rows.
+
 Prints one JSON line (last line of stdout).  `value` is the effective HBM
 throughput of a step: the algorithmic bytes of the three calls (each input
 read once, each output written once) divided by the measured time per step.
@@ -40,6 +46,7 @@ KERNEL_SOURCES = {
     "combine": ["ep_combine.hip", "ep_device.h", "ep_internal.h"],
     "dispatch": ["ep_dispatch.hip", "ep_device.h", "ep_internal.h"],
     "layout": ["ep_layout.hip", "ep_device.h", "ep_internal.h"],
+    "ll_dispatch": ["ep_dispatch.hip", "ep_device.h", "ep_internal.h"],
 }
 
 
@@ -58,6 +65,17 @@ def algorithmic_bytes(T, H, E, P, K, fp8):
     combine = R * H * 2 + R * 4 + R * 4 + T * H * 2
     return dict(layout=layout, dispatch=dispatch, combine=combine,
                 total=layout + dispatch + combine)
+
+
+def ll_algorithmic_bytes(T, H, E, K, C, fp8, filled):
+    """The decode path's bytes: x and the routing read once, the ``filled``
+    receive rows (plus scales) written once, the whole row map and the
+    counts written; combine reads the filled rows."""
+    G = H // 128
+    dispatch = T * H * 2 + T * K * 8 + filled * H * (1 if fp8 else 2) \
+        + (filled * G * 4 if fp8 else 0) + E * C * 4 + T * K * 4 + E * 4 + 8
+    combine = filled * H * 2 + T * K * 4 + T * K * 4 + T * H * 2
+    return dict(ll_dispatch=dispatch, combine=combine, total=dispatch + combine)
 
 
 def kernel_source_hash(kernel):
@@ -88,15 +106,26 @@ def pct(a, q):
     return float(np.percentile(np.asarray(a), q)) if len(a) else None
 
 
-def cpu_baseline(wl_case, nbytes, seconds):
+def cpu_baseline(wl_case, nbytes, seconds, capacity=None):
     """The CPU oracle (single-threaded C) on the same workload, repeated until
-    `seconds` of CPU work have accumulated (at least one full pass)."""
+    `seconds` of CPU work have accumulated (at least one full pass).  With a
+    capacity it runs the oracle's fixed-capacity path instead (its combine on
+    expert outputs of the layout's shape)."""
     import oracle
+    from combine_ep_get_dispatch_amd import workloads as wl
     passes, t_total = 0, 0.0
+    y_ll = None
+    if capacity is not None:
+        y_ll = wl.normal_bf16(300 + wl.CONFIGS[wl_case.name]["c"],
+                              (wl_case.E * capacity, wl_case.H))
     while True:
         t0 = time.perf_counter()
-        oracle.run(wl_case.topk_idx, wl_case.x_bits, wl_case.E, wl_case.P, wl_case.fp8,
-                   wl_case.y_bits, wl_case.topk_weights)
+        if capacity is None:
+            oracle.run(wl_case.topk_idx, wl_case.x_bits, wl_case.E, wl_case.P, wl_case.fp8,
+                       wl_case.y_bits, wl_case.topk_weights)
+        else:
+            oracle.run_ll(wl_case.topk_idx, wl_case.x_bits, wl_case.E, capacity, wl_case.fp8,
+                          y_ll, wl_case.topk_weights)
         t_total += time.perf_counter() - t0
         passes += 1
         log("cpu oracle pass %d: %.2f s total" % (passes, t_total))
@@ -104,9 +133,11 @@ def cpu_baseline(wl_case, nbytes, seconds):
             break
     return {"value": round(nbytes * passes / t_total / 1e9, 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": "%d full pass(es) of the %s workload (T=%d), layout+dispatch+combine, "
-                      "single-threaded C oracle, %.1f s" % (passes, wl_case.name, wl_case.T,
-                                                           t_total),
+            "sample": "%d full pass(es) of the %s workload (T=%d), %s, "
+                      "single-threaded C oracle, %.1f s"
+                      % (passes, wl_case.name, wl_case.T,
+                         "layout+dispatch+combine" if capacity is None else
+                         "fixed-capacity (C=%d) dispatch+combine" % capacity, t_total),
             "us_per_step": round(t_total / passes * 1e6, 1)}
 
 
@@ -115,13 +146,22 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="prefill")
+    ap.add_argument("--config", default=None,
+                    help="workload (default: prefill; decode with --low-latency)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-copy-ceiling", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph and replayed")
+    ap.add_argument("--graph-steps", type=int, default=10,
+                    help="steps captured back to back in the one graph (--graph)")
+    ap.add_argument("--low-latency", action="store_true",
+                    help="time the single-launch fixed-capacity decode path")
+    ap.add_argument("--capacity", type=int, default=0,
+                    help="rows per expert for --low-latency (default: T)")
     args = ap.parse_args()
+    if args.config is None:
+        args.config = "decode" if args.low_latency else "prefill"
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -145,36 +185,53 @@ def main():
     case = wl.make(args.config)
     T, H, E, P, K, fp8 = case.T, case.H, case.E, case.P, case.K, case.fp8
     R = T * K
+    C = args.capacity or T
+    if args.low_latency and T * K > ep.LL_MAX_SLOTS:
+        print("--low-latency takes at most %d routing slots; %s has %d"
+              % (ep.LL_MAX_SLOTS, args.config, T * K), file=sys.stderr)
+        sys.exit(2)
     idx = torch.from_numpy(case.topk_idx).to(dev)
     x = torch.from_numpy(case.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    y = torch.from_numpy(case.y_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     w = torch.from_numpy(case.topk_weights).to(dev)
-    ws = ep.new_workspace(T, K, E, P, dev)
-    lay = ep.Layout(torch.empty(E, dtype=torch.int32, device=dev),
-                    torch.empty(P, dtype=torch.int32, device=dev),
-                    torch.empty((T, P), dtype=torch.uint8, device=dev),
-                    torch.empty(E + 1, dtype=torch.int32, device=dev),
-                    torch.empty(P + 1, dtype=torch.int32, device=dev), ws)
-    disp = ep.Dispatched(
-        torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev),
-        torch.empty((R, H // 128), dtype=torch.float32, device=dev) if fp8 else None,
-        torch.empty(R, dtype=torch.int32, device=dev),
-        torch.empty((T, K), dtype=torch.int32, device=dev))
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if args.low_latency:
+        # expert outputs laid out like the fixed-capacity receive rows
+        y = torch.from_numpy(wl.normal_bf16(300 + wl.CONFIGS[args.config]["c"], (E * C, H))
+                             .view(np.int16)).to(dev).view(torch.bfloat16)
+        lld = ep.LowLatencyDispatched(
+            torch.empty(E, dtype=torch.int32, device=dev),
+            torch.empty((E * C, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev),
+            torch.empty((E * C, H // 128), dtype=torch.float32, device=dev) if fp8 else None,
+            torch.empty(E * C, dtype=torch.int32, device=dev),
+            torch.empty((T, K), dtype=torch.int32, device=dev),
+            torch.empty(1, dtype=torch.int64, device=dev))
+        calls = [("ll_dispatch", lambda: ep.low_latency_dispatch(x, idx, E, C, fp8=fp8, out=lld)),
+                 ("combine", lambda: ep.combine(y, lld.dst_row, w, out=out))]
+    else:
+        y = torch.from_numpy(case.y_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        ws = ep.new_workspace(T, K, E, P, dev)
+        lay = ep.Layout(torch.empty(E, dtype=torch.int32, device=dev),
+                        torch.empty(P, dtype=torch.int32, device=dev),
+                        torch.empty((T, P), dtype=torch.uint8, device=dev),
+                        torch.empty(E + 1, dtype=torch.int32, device=dev),
+                        torch.empty(P + 1, dtype=torch.int32, device=dev), ws)
+        disp = ep.Dispatched(
+            torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev),
+            torch.empty((R, H // 128), dtype=torch.float32, device=dev) if fp8 else None,
+            torch.empty(R, dtype=torch.int32, device=dev),
+            torch.empty((T, K), dtype=torch.int32, device=dev))
+        calls = [("layout", lambda: ep.get_dispatch_layout(idx, E, P, workspace=ws, out=lay)),
+                 ("dispatch", lambda: ep.dispatch(x, idx, E, P, ws, fp8=fp8, out=disp)),
+                 ("combine", lambda: ep.combine(y, disp.dst_row, w, out=out))]
     torch.cuda.synchronize()
 
     def step(ev=None):
+        for i, (_, fn) in enumerate(calls):
+            if ev is not None:
+                ev[i].record()
+            fn()
         if ev is not None:
-            ev[0].record()
-        ep.get_dispatch_layout(idx, E, P, workspace=ws, out=lay)
-        if ev is not None:
-            ev[1].record()
-        ep.dispatch(x, idx, E, P, ws, fp8=fp8, out=disp)
-        if ev is not None:
-            ev[2].record()
-        ep.combine(y, disp.dst_row, w, out=out)
-        if ev is not None:
-            ev[3].record()
+            ev[len(calls)].record()
 
     log("warmup %d" % args.warmup)
     for _ in range(args.warmup):
@@ -194,25 +251,30 @@ def main():
     log("timed %d steps: %.2f us/step" % (args.steps, ms_per_step * 1e3))
 
     # ---- per-kernel breakdown: events around every call, same stream --------
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    nc = len(calls)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nc + 1)]
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    lay_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
-    dis_us = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
-    com_us = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
-    tot_us = [e[0].elapsed_time(e[3]) * 1e3 for e in evs]
+    call_us = {name: [e[i].elapsed_time(e[i + 1]) * 1e3 for e in evs]
+               for i, (name, _) in enumerate(calls)}
+    tot_us = [e[0].elapsed_time(e[nc]) * 1e3 for e in evs]
 
-    # ---- combine launched back to back on its stream: its kernel duration ---
+    # ---- the dominant kernel launched back to back on its stream ------------
+    # (combine on the offsets path; the single dispatch launch on the decode
+    # path, where it is the larger of the two)
+    dom_name = "ll_dispatch" if args.low_latency else "combine"
+    dom_fn = dict(calls)[dom_name]
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     c0.record()
     for _ in range(args.steps):
-        ep.combine(y, disp.dst_row, w, out=out)
+        dom_fn()
     c1.record()
     torch.cuda.synchronize()
-    com_b2b_us = c0.elapsed_time(c1) / args.steps * 1e3
+    dom_b2b_us = c0.elapsed_time(c1) / args.steps * 1e3
 
     # ---- the same step captured once in a HIP graph and replayed -----------
     graph_us = None
@@ -225,21 +287,27 @@ def main():
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
-            step()
-        for _ in range(args.warmup):
+            for _ in range(args.graph_steps):
+                step()
+        for _ in range(max(1, args.warmup // args.graph_steps)):
             g.replay()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        replays = max(1, args.steps // args.graph_steps)
         torch.cuda.synchronize()
         g0.record()
-        for _ in range(args.steps):
+        for _ in range(replays):
             g.replay()
         g1.record()
         torch.cuda.synchronize()
-        graph_us = g0.elapsed_time(g1) / args.steps * 1e3
-        log("graph replay: %.2f us/step" % graph_us)
+        graph_us = g0.elapsed_time(g1) / (replays * args.graph_steps) * 1e3
+        log("graph replay (%d steps per graph): %.2f us/step" % (args.graph_steps, graph_us))
         del g
 
-    nb = algorithmic_bytes(T, H, E, P, K, fp8)
+    if args.low_latency:
+        filled = int((lld.recv_src_token >= 0).sum().item())
+        nb = ll_algorithmic_bytes(T, H, E, K, C, fp8, filled)
+    else:
+        nb = algorithmic_bytes(T, H, E, P, K, fp8)
     value = nb["total"] / (ms_per_step * 1e-3) / 1e9
 
     # ---- copy ceiling (measured) ---------------------------------------------
@@ -260,22 +328,25 @@ def main():
         del a, b
         log("copy ceiling %.0f GB/s" % copy_gbs)
 
-    com_avg = float(np.mean(com_us))
-    achieved = nb["combine"] / (com_b2b_us * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": "combine_kernel<%d>" % K if K in (1, 2, 4, 6, 8)
-                else "combine_kernel<0>",
+    achieved = nb[dom_name] / (dom_b2b_us * 1e-6) / 1e9
+    if args.low_latency:
+        kname = "ll_dispatch_kernel<%s>" % ("true" if fp8 else "false")
+    else:
+        kname = "combine_kernel<%d>" % (K if K in (1, 2, 4, 6, 8) else 0)
+    roofline = {"bound": "hbm", "kernel": kname,
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic("combine", args.config),
-                "algorithmic_bytes_per_launch": nb["combine"],
-                "avg_launch_us": round(com_b2b_us, 2),
+                "traffic": measured_traffic(dom_name, args.config + ("-ll" if args.low_latency
+                                                                    else "")),
+                "algorithmic_bytes_per_launch": nb[dom_name],
+                "avg_launch_us": round(dom_b2b_us, 2),
                 "timing": "HIP events around %d back-to-back launches on the launch stream"
                           % args.steps,
-                "avg_launch_us_in_step": round(com_avg, 2)}
+                "avg_launch_us_in_step": round(float(np.mean(call_us[dom_name])), 2)}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, nb["total"], args.cpu_seconds)
+        cpu = cpu_baseline(case, nb["total"], args.cpu_seconds, C if args.low_latency else None)
 
     def q(a):
         return {"p10": round(pct(a, 10), 2), "p50": round(pct(a, 50), 2),
@@ -292,7 +363,8 @@ def main():
         "us_per_call": round(ms_per_step * 1e3, 2),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "graph_replay": ({"us_per_call": round(graph_us, 2),
-                          "gbs": round(nb["total"] / (graph_us * 1e-6) / 1e9, 1)}
+                          "gbs": round(nb["total"] / (graph_us * 1e-6) / 1e9, 1),
+                          "steps_per_graph": args.graph_steps}
                          if graph_us else None),
         "higher_is_better": True,
         "scaling": "weak",
@@ -303,13 +375,16 @@ def main():
                       "accumulate": "fp32"},
         "data": "synthetic",
         "config": {"workload": "%s: %d tokens x %d hidden, top-%d of %d experts, %d partitions, "
-                               "%s dispatch" % (args.config, T, H, K, E, P,
-                                                "FP8 E4M3 per-128" if fp8 else "bf16"),
+                               "%s dispatch%s" % (args.config, T, H, K, E, P,
+                                                  "FP8 E4M3 per-128" if fp8 else "bf16",
+                                                  ", single-launch fixed capacity %d per expert"
+                                                  % C if args.low_latency else ""),
                    "tokens": T, "hidden": H, "experts": E, "partitions": P, "topk": K,
-                   "fp8_dispatch": fp8, "parallelism": "single GPU"},
+                   "fp8_dispatch": fp8, "parallelism": "single GPU",
+                   "path": "low_latency" if args.low_latency else "offsets"},
         "algorithmic_bytes": nb,
-        "breakdown_us": {"layout": q(lay_us), "dispatch": q(dis_us), "combine": q(com_us),
-                         "step_with_events": q(tot_us)},
+        "breakdown_us": dict({name: q(v) for name, v in call_us.items()},
+                             step_with_events=q(tot_us)),
         "copy_ceiling_gbs": round(copy_gbs, 1) if copy_gbs else None,
         "pct_of_copy_ceiling": round(100 * value / copy_gbs, 2) if copy_gbs else None,
         "roofline": roofline,

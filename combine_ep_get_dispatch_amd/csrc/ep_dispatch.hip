@@ -29,85 +29,135 @@
 namespace ep {
 namespace {
 
-// Scatter token t (one workgroup): quantise or copy its H channels and write
-// them to the K destination rows held by lanes 0..K-1 of `drow` (-1 = none).
-// s_scale is G floats of LDS (FP8 only).
+// One lane's share of one 1024-channel chunk of a token, ready to store.
+// FP8: lane l holds the 16 codes of channels [16l, 16l + 16) of the chunk (its
+// 128-channel group is lanes 8g .. 8g+7; the group's scale goes to s_scale).
+// bf16: lane l holds channels [8l, 8l + 8) and [512 + 8l, 512 + 8l + 8), so
+// every load and store instruction covers 1 KiB of consecutive bytes.
+struct ChunkData {
+    uint4 a, b;
+};
+
+// The chunk's raw bf16 words as loaded (FP8: 16 channels per lane; bf16:
+// the two 8-channel runs), kept apart from the conversion so that a kernel
+// can issue the loads early and convert once it has waited for them.  The
+// loads are branch-free: a lane past the end of the row loads the row's last
+// 16 bytes instead (always in bounds), and everything downstream ignores it
+// (finish_chunk and store_chunk test h < H), so the compiler can wait for
+// other loads without waiting for these.
+template <bool FP8>
+__device__ __forceinline__ ChunkData load_raw(const uint16_t* __restrict__ x, int H, int t,
+                                              int c) {
+    const int lane = threadIdx.x & 63;
+    const uint16_t* xs = x + (int64_t)t * H;
+    ChunkData d;
+    if constexpr (FP8) {
+        const int h0 = c * kDispatchChunk + lane * 16;
+        const int hc = h0 < H ? h0 : H - 16;   // H % 128 == 0
+        d.a = load_nt(xs + hc);                // each byte of x is used once
+        d.b = load_nt(xs + hc + 8);
+    } else {
+        const int ha = c * kDispatchChunk + lane * 8;
+        const int hb = ha + kDispatchChunk / 2;
+        d.a = *reinterpret_cast<const uint4*>(xs + (ha < H ? ha : H - 8));   // H % 8 == 0
+        d.b = *reinterpret_cast<const uint4*>(xs + (hb < H ? hb : H - 8));
+    }
+    return d;
+}
+
+// Raw words -> what store_chunk writes: the E4M3 codes in .a (and the group
+// scale in s_scale) for FP8; unchanged for bf16.
+template <bool FP8>
+__device__ __forceinline__ ChunkData finish_chunk(const ChunkData& raw, int H, int c,
+                                                  float* s_scale) {
+    if constexpr (!FP8) {
+        return raw;
+    } else {
+        const int lane = threadIdx.x & 63;
+        const int h0 = c * kDispatchChunk + lane * 16;
+        const uint32_t w[8] = {raw.a.x, raw.a.y, raw.a.z, raw.a.w,
+                               raw.b.x, raw.b.y, raw.b.z, raw.b.w};
+        float f[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            f[2 * i] = bf16_lo(w[i]);
+            f[2 * i + 1] = bf16_hi(w[i]);
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+        amax = group8_max(amax);
+        const float ac = fmaxf(amax, 1e-4f);
+        const float inv = 448.0f / ac;
+        const float scale = ac / 448.0f;
+        ChunkData d;
+        d.a.x = e4m3x4_hw(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+        d.a.y = e4m3x4_hw(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+        d.a.z = e4m3x4_hw(f[8] * inv, f[9] * inv, f[10] * inv, f[11] * inv);
+        d.a.w = e4m3x4_hw(f[12] * inv, f[13] * inv, f[14] * inv, f[15] * inv);
+        d.b = make_uint4(0, 0, 0, 0);
+        if (h0 < H && (lane & 7) == 0) s_scale[h0 >> 7] = scale;
+        return d;
+    }
+}
+
+template <bool FP8>
+__device__ __forceinline__ ChunkData load_chunk(const uint16_t* __restrict__ x, int H, int t,
+                                                int c, float* s_scale) {
+    return finish_chunk<FP8>(load_raw<FP8>(x, H, t, c), H, c, s_scale);
+}
+
+// Store one chunk to the K destination rows held by lanes 0..K-1 of `drow`
+// (-1 = none).  FP8 rows are written through L2 (device-scope stores) and
+// bf16 rows non-temporally: each measured fastest for its row size.
+template <bool FP8>
+__device__ __forceinline__ void store_chunk(const ChunkData& d, int H, int K, int c, int drow,
+                                            void* __restrict__ recv_x) {
+    const int lane = threadIdx.x & 63;
+    if constexpr (FP8) {
+        const int h0 = c * kDispatchChunk + lane * 16;
+        const bool act = h0 < H;
+        for (int k = 0; k < K; ++k) {
+            const int r = __builtin_amdgcn_readlane(drow, k);
+            if (r < 0) continue;
+            if (act) store_wt(static_cast<uint8_t*>(recv_x) + (int64_t)r * H + h0, d.a);
+        }
+    } else {
+        const int ha = c * kDispatchChunk + lane * 8;
+        const int hb = ha + kDispatchChunk / 2;
+        for (int k = 0; k < K; ++k) {
+            const int r = __builtin_amdgcn_readlane(drow, k);
+            if (r < 0) continue;
+            uint16_t* dst = static_cast<uint16_t*>(recv_x) + (int64_t)r * H;
+            if (ha < H) store_nt(dst + ha, d.a);
+            if (hb < H) store_nt(dst + hb, d.b);
+        }
+    }
+}
+
+// Scatter token t (one workgroup of nw waves): wave w handles chunks w, w+nw,
+// ...; `first` is chunk `wave`, already loaded (when wave < nchunk).  FP8: the
+// token's G scales are gathered in s_scale (LDS) and each destination's scale
+// row then goes out as one contiguous store.
 template <bool FP8>
 __device__ __forceinline__ void scatter_token(const uint16_t* __restrict__ x, int H, int K, int t,
-                                              int drow, void* __restrict__ recv_x,
+                                              int drow, const ChunkData& first,
+                                              void* __restrict__ recv_x,
                                               float* __restrict__ recv_scales, float* s_scale,
                                               int nchunk) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nw = blockDim.x >> 6;
-    if constexpr (FP8) {
-        // Lane l quantises channels [16l, 16l + 16) of the chunk: its 128-channel
-        // group is lanes 8g .. 8g+7, and its 16 codes are one 16-byte store.
-        for (int c = wave; c < nchunk; c += nw) {
-            const int h0 = c * kDispatchChunk + lane * 16;
-            const bool act = h0 < H;       // H % 128 == 0: all 16 channels or none
-            const uint16_t* xs = x + (int64_t)t * H + h0;
-            uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-            if (act) {
-                v0 = load_nt(xs);
-                v1 = load_nt(xs + 8);
-            }
-            const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-            float f[16];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                f[2 * i] = bf16_lo(w[i]);
-                f[2 * i + 1] = bf16_hi(w[i]);
-            }
-            float amax = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-            amax = group8_max(amax);
-            const float ac = fmaxf(amax, 1e-4f);
-            const float inv = 448.0f / ac;
-            const float scale = ac / 448.0f;
-            uint4 q;
-            q.x = e4m3x4_hw(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
-            q.y = e4m3x4_hw(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
-            q.z = e4m3x4_hw(f[8] * inv, f[9] * inv, f[10] * inv, f[11] * inv);
-            q.w = e4m3x4_hw(f[12] * inv, f[13] * inv, f[14] * inv, f[15] * inv);
-            if (act && (lane & 7) == 0) s_scale[h0 >> 7] = scale;
-            for (int k = 0; k < K; ++k) {
-                const int d = __builtin_amdgcn_readlane(drow, k);
-                if (d < 0) continue;
-                if (act) store_wt(static_cast<uint8_t*>(recv_x) + (int64_t)d * H + h0, q);
-            }
-        }
-    } else {
-        // Lane l copies channels [8l, 8l + 8) and [512 + 8l, 512 + 8l + 8) of
-        // the chunk, so every load and store instruction covers 1 KiB of
-        // consecutive bytes (whole cache lines).  Non-temporal stores measured
-        // fastest for these rows (bf16 receive rows are twice the FP8 bytes).
-        for (int c = wave; c < nchunk; c += nw) {
-            const int ha = c * kDispatchChunk + lane * 8;
-            const int hb = ha + kDispatchChunk / 2;
-            const bool act_a = ha < H;     // H % 8 == 0: all 8 channels or none
-            const bool act_b = hb < H;
-            const uint16_t* xs = x + (int64_t)t * H;
-            uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
-            if (act_a) va = *reinterpret_cast<const uint4*>(xs + ha);
-            if (act_b) vb = *reinterpret_cast<const uint4*>(xs + hb);
-            for (int k = 0; k < K; ++k) {
-                const int d = __builtin_amdgcn_readlane(drow, k);
-                if (d < 0) continue;
-                uint16_t* dst = static_cast<uint16_t*>(recv_x) + (int64_t)d * H;
-                if (act_a) store_nt(dst + ha, va);
-                if (act_b) store_nt(dst + hb, vb);
-            }
-        }
-    }
+    if (wave < nchunk) store_chunk<FP8>(first, H, K, wave, drow, recv_x);
+    for (int c = wave + nw; c < nchunk; c += nw)
+        store_chunk<FP8>(load_chunk<FP8>(x, H, t, c, s_scale), H, K, c, drow, recv_x);
     if constexpr (FP8) {
         __syncthreads();
         const int G = H >> 7;
         for (int k = wave; k < K; k += nw) {   // one wave per destination scale row
-            const int d = __builtin_amdgcn_readlane(drow, k);
-            if (d < 0) continue;
-            for (int g = lane; g < G; g += 64) recv_scales[(int64_t)d * G + g] = s_scale[g];
+            const int r = __builtin_amdgcn_readlane(drow, k);
+            if (r < 0) continue;
+            for (int g = lane; g < G; g += 64) recv_scales[(int64_t)r * G + g] = s_scale[g];
         }
     }
 }
@@ -122,7 +172,8 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void dispatch_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = blockIdx.x;
 
-    // Destination row of slot k = lane (K <= 64).
+    // Destination row of slot k = lane (K <= 64).  (Loading x before these
+    // rows are known measured slower, here and in the decode kernel.)
     int drow = -1;
     if (lane < K) {
         drow = rows[(int64_t)t * K + lane];
@@ -135,7 +186,9 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void dispatch_kernel(
         const int r = t * K + lane;
         if (r >= hdr->num_valid) recv_src[r] = -1;
     }
-    scatter_token<FP8>(x, H, K, t, drow, recv_x, recv_scales, s_scale, nchunk);
+    ChunkData first;
+    if (wave < nchunk) first = load_chunk<FP8>(x, H, t, wave, s_scale);
+    scatter_token<FP8>(x, H, K, t, drow, first, recv_x, recv_scales, s_scale, nchunk);
 }
 
 // Decode dispatch into fixed-capacity receive rows, in one launch (expert e
@@ -166,6 +219,23 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void ll_dispatch_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t = blockIdx.x;
 
+    // This token's own ids (lane k holds slot k) and the first round of the
+    // routing scan are loaded together (T >= 1 here and t < T; branch-free,
+    // clamped in-bounds loads whose extra lanes are discarded).  The token's
+    // row is loaded only once its destinations are known: loading it first
+    // measured slower.
+    int64_t own = idx[(int64_t)t * K + (lane < K ? lane : K - 1)];
+    if (lane >= K) own = -1;
+    const int n = T * K;
+    const int before = t * K;
+    int64_t v[kLlScanUnroll];
+#pragma unroll
+    for (int j = 0; j < kLlScanUnroll; ++j) {
+        const int i = tid + j * nthr;
+        v[j] = idx[i < n ? i : n - 1];
+        if (i >= n) v[j] = -1;
+    }
+
     for (int e = tid; e < E; e += nthr) {
         h_pre[e] = 0;
         h_all[e] = 0;
@@ -173,17 +243,30 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void ll_dispatch_kernel(
     if (tid == 0) s_inv = 0;
     __syncthreads();
 
-    const int n = T * K;
-    const int before = t * K;
+    // The first round (all of it up to kLlScanUnroll * blockDim slots) is
+    // straight-line code; larger inputs loop for the rest.
     int inv = 0;
-    for (int i = tid; i < n; i += nthr) {
-        const int64_t v = idx[i];
-        if (v >= 0 && v < E) {
-            atomicAdd(&h_all[v], 1);
-            if (i < before) atomicAdd(&h_pre[v], 1);
-        } else if (v != -1) {
-            ++inv;
+    auto count = [&](int i0) {
+#pragma unroll
+        for (int j = 0; j < kLlScanUnroll; ++j) {
+            const int i = i0 + j * nthr;
+            if (v[j] >= 0 && v[j] < E) {
+                atomicAdd(&h_all[v[j]], 1);
+                if (i < before) atomicAdd(&h_pre[v[j]], 1);
+            } else if (v[j] != -1) {
+                ++inv;
+            }
         }
+    };
+    count(tid);
+    for (int i0 = tid + kLlScanUnroll * nthr; i0 < n; i0 += kLlScanUnroll * nthr) {
+#pragma unroll
+        for (int j = 0; j < kLlScanUnroll; ++j) {
+            const int i = i0 + j * nthr;
+            v[j] = idx[i < n ? i : n - 1];
+            if (i >= n) v[j] = -1;
+        }
+        count(i0);
     }
     if (blockIdx.x == 0 && inv != 0) atomicAdd(&s_inv, inv);
     __syncthreads();
@@ -191,12 +274,8 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void ll_dispatch_kernel(
     // Row of slot k = lane: expert e's slots of earlier tokens, plus the
     // earlier slots of this token with the same expert.
     int drow = -1;
-    if (t < T) {
-        int e = -1;
-        if (lane < K) {
-            const int64_t v = idx[(int64_t)t * K + lane];
-            if (v >= 0 && v < E) e = (int)v;
-        }
+    {
+        const int e = (own >= 0 && own < E) ? (int)own : -1;
         int dup = 0;
         for (int j = 0; j < K; ++j) {
             const int ej = __builtin_amdgcn_readlane(e, j);
@@ -219,7 +298,19 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void ll_dispatch_kernel(
     }
     if (blockIdx.x == 0 && tid == 0 && num_invalid) *num_invalid = s_inv;
 
-    if (t < T) scatter_token<FP8>(x, H, K, t, drow, recv_x, recv_scales, s_scale, nchunk);
+    ChunkData first;
+    if (wave < nchunk) first = load_chunk<FP8>(x, H, t, wave, s_scale);
+    scatter_token<FP8>(x, H, K, t, drow, first, recv_x, recv_scales, s_scale, nchunk);
+}
+
+// T = 0: every count is 0, every row unfilled, nothing invalid.
+__global__ void ll_empty_kernel(int E, int C, int32_t* __restrict__ cnt_e,
+                                int32_t* __restrict__ recv_src,
+                                int64_t* __restrict__ num_invalid) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < E) cnt_e[i] = 0;
+    if (i < (int64_t)E * C) recv_src[i] = -1;
+    if (i == 0 && num_invalid) *num_invalid = 0;
 }
 
 }  // namespace
@@ -252,10 +343,16 @@ hipError_t launch_ll_dispatch(const uint16_t* x, const int64_t* idx, int T, int 
                               int32_t* recv_src, int32_t* dst_row, int64_t* num_invalid,
                               hipStream_t s) {
     const int nchunk = (H + kDispatchChunk - 1) / kDispatchChunk;
-    int nw = nchunk < kDispatchMaxThreads / 64 ? nchunk : kDispatchMaxThreads / 64;
-    if (nw < kLlMinWaves) nw = kLlMinWaves;     // more threads for the routing scan
+    const int nw = kLlWaves;
+    static_assert(kLlWaves * 64 <= kDispatchMaxThreads, "block too large");
     const size_t lds = ll_dispatch_lds_bytes(E, H, fp8);
-    const unsigned grid = T > 0 ? (unsigned)T : 1u;
+    if (T == 0) {
+        const int64_t rows = (int64_t)E * C > E ? (int64_t)E * C : E;
+        hipLaunchKernelGGL(ll_empty_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
+                           E, C, cnt_e, recv_src, num_invalid);
+        return hipGetLastError();
+    }
+    const unsigned grid = (unsigned)T;
     if (fp8)
         hipLaunchKernelGGL(ll_dispatch_kernel<true>, dim3(grid), dim3(64 * nw), lds, s, x, idx, T,
                            H, K, E, C, cnt_e, recv_x, recv_scales, recv_src, dst_row,

@@ -81,11 +81,14 @@ hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K, bool fp8, voi
                            float* recv_scales, int32_t* recv_src, int32_t* dst_row,
                            const void* ws, const WsMap& m, hipStream_t s);
 
-// Fixed-capacity (decode) dispatch: one launch, one workgroup per token (one
-// workgroup when T = 0), at least kLlMinWaves waves so the routing scan that
-// every workgroup does has threads enough.  LDS: two [E] int histograms and,
-// for FP8, the token's G scales.
-constexpr int kLlMinWaves = 4;
+// Fixed-capacity (decode) dispatch: one launch, one workgroup per token (T = 0
+// takes a small fill kernel instead) of kLlWaves waves, so that the routing scan every
+// workgroup does needs few rounds of loads (kLlScanUnroll in flight per
+// thread: one round up to 4096 slots); waves past the token's channel chunks
+// only take part in the scan.  LDS: two [E] int histograms and, for FP8, the
+// token's G scales.
+constexpr int kLlWaves = 16;
+constexpr int kLlScanUnroll = 4;
 
 size_t ll_dispatch_lds_bytes(int E, int H, bool fp8);
 
