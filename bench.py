@@ -1,8 +1,10 @@
 """Benchmark: MoE dispatch + combine on one MI355X.
 
-One step = the whole path on one batch: ep_get_dispatch_layout ->
-ep_dispatch -> ep_combine, on seeded synthetic routing and activations that
-are resident in HBM before timing starts.  The default workload is the
+One step = the whole path on one batch: ep_layout_dispatch (the layout and
+the dispatch in one call, two kernel launches) -> ep_combine, on seeded
+synthetic routing and activations that are resident in HBM before timing
+starts (`--two-calls` times ep_get_dispatch_layout -> ep_dispatch ->
+ep_combine instead).  The default workload is the
 prefill configuration (4096 tokens x 7168 hidden, top-8 of 256 experts with
 group-limited gating, 64 partitions, FP8 E4M3 dispatch with per-128 scales,
 bf16 weighted combine).
@@ -155,6 +157,8 @@ def main():
                     help="also time the step captured in a HIP graph and replayed")
     ap.add_argument("--graph-steps", type=int, default=10,
                     help="steps captured back to back in the one graph (--graph)")
+    ap.add_argument("--two-calls", action="store_true",
+                    help="layout and dispatch as two calls instead of ep_layout_dispatch")
     ap.add_argument("--low-latency", action="store_true",
                     help="time the single-launch fixed-capacity decode path")
     ap.add_argument("--capacity", type=int, default=0,
@@ -220,9 +224,13 @@ def main():
             torch.empty((R, H // 128), dtype=torch.float32, device=dev) if fp8 else None,
             torch.empty(R, dtype=torch.int32, device=dev),
             torch.empty((T, K), dtype=torch.int32, device=dev))
-        calls = [("layout", lambda: ep.get_dispatch_layout(idx, E, P, workspace=ws, out=lay)),
-                 ("dispatch", lambda: ep.dispatch(x, idx, E, P, ws, fp8=fp8, out=disp)),
-                 ("combine", lambda: ep.combine(y, disp.dst_row, w, out=out))]
+        if args.two_calls:
+            calls = [("layout", lambda: ep.get_dispatch_layout(idx, E, P, workspace=ws, out=lay)),
+                     ("dispatch", lambda: ep.dispatch(x, idx, E, P, ws, fp8=fp8, out=disp))]
+        else:
+            calls = [("layout_dispatch", lambda: ep.layout_dispatch(
+                x, idx, E, P, workspace=ws, fp8=fp8, out_layout=lay, out=disp))]
+        calls.append(("combine", lambda: ep.combine(y, disp.dst_row, w, out=out)))
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -381,7 +389,8 @@ def main():
                                                   % C if args.low_latency else ""),
                    "tokens": T, "hidden": H, "experts": E, "partitions": P, "topk": K,
                    "fp8_dispatch": fp8, "parallelism": "single GPU",
-                   "path": "low_latency" if args.low_latency else "offsets"},
+                   "path": "low_latency" if args.low_latency else
+                           ("offsets, two calls" if args.two_calls else "offsets, one call")},
         "algorithmic_bytes": nb,
         "breakdown_us": dict({name: q(v) for name, v in call_us.items()},
                              step_with_events=q(tot_us)),

@@ -191,6 +191,93 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void dispatch_kernel(
     scatter_token<FP8>(x, H, K, t, drow, first, recv_x, recv_scales, s_scale, nchunk);
 }
 
+// Dispatch that also finishes the layout (after layout_count_kernel<true>).
+// Slot (t,k) of expert e, in token block b, with rank r inside the block:
+//   row = expert_offsets[e] + (rows of e in blocks < b) + r
+//       = sum over blocks j of pre[j][e] + sum over j < b of cnt[j][e] + r,
+// and N = sum over j of pre[j][E].  Thread i = k * S + j (S = blocks rounded
+// up to a power of two) loads slot k's packed row and then block j's term
+// for it (k = K: block j's term of N): one round of L2 loads after the row
+// load, spread over (K+1)*S threads.  A shuffle reduction over each S-lane
+// segment gives the row, which reaches the other waves through LDS (one
+// barrier).  Workgroup 0 also writes the counts, offsets and header.
+template <bool FP8>
+__global__ __launch_bounds__(kDispatchMaxThreads) void layout_dispatch_kernel(
+    const uint16_t* __restrict__ x, int H, int K, int E, int P, int Ep, int TB, int nb,
+    int seg_log2, const int* __restrict__ cnt, const int* __restrict__ pre,
+    const int* __restrict__ pcnt, const int* __restrict__ inv, const int* __restrict__ rows,
+    WsHeader* __restrict__ hdr, int32_t* __restrict__ cnt_e, int32_t* __restrict__ cnt_p,
+    int32_t* __restrict__ off_e, int32_t* __restrict__ off_p, void* __restrict__ recv_x,
+    float* __restrict__ recv_scales, int32_t* __restrict__ recv_src,
+    int32_t* __restrict__ dst_row, int nchunk) {
+    extern __shared__ float s_scale[];   // [G] scales of this token (FP8)
+    __shared__ int s_row[64];            // receive row of slot k (K <= 64)
+    __shared__ int s_n;                  // N
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int t = blockIdx.x;
+
+    {
+        const int b = t / TB;
+        const int S = 1 << seg_log2;     // segment lanes, S >= nb, S <= 64
+        const int k = tid >> seg_log2;
+        const int j = tid & (S - 1);
+        int pk = -1, v = 0;
+        if (k < K) {
+            pk = rows[(int64_t)t * K + k];
+            if (pk >= 0 && j < nb) {
+                const int e = pk >> kRankBits;
+                v = pre[(int64_t)j * (E + 1) + e];
+                if (j < b) v += cnt[(int64_t)j * E + e];
+            }
+        } else if (k == K && j < nb) {
+            v = pre[(int64_t)j * (E + 1) + E];
+        }
+        for (int o = S >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+        if (j == 0) {
+            if (k < K) s_row[k] = pk >= 0 ? v + (pk & ((1 << kRankBits) - 1)) : -1;
+            else if (k == K) s_n = v;
+        }
+    }
+    __syncthreads();
+    const int drow = lane < K ? s_row[lane] : -1;
+    if (wave == 0 && lane < K) {
+        dst_row[(int64_t)t * K + lane] = drow;
+        if (drow >= 0) recv_src[drow] = t;
+        const int r = t * K + lane;        // rows past the last valid one belong to no token
+        if (r >= s_n) recv_src[r] = -1;
+    }
+    if (t == 0 && tid == 0) hdr->num_valid = s_n;
+
+    if (t == 0) {                          // the layout's own outputs
+        for (int e = tid; e <= E; e += blockDim.x) {
+            int c = 0, o = 0;
+            for (int j = 0; j < nb; ++j) {
+                o += pre[(int64_t)j * (E + 1) + e];
+                if (e < E) c += cnt[(int64_t)j * E + e];
+            }
+            off_e[e] = o;
+            if (e < E) cnt_e[e] = c;
+            if (e % Ep == 0) off_p[e / Ep] = o;     // e = P*Ep = E gives off_p[P] = N
+        }
+        for (int p = tid; p < P; p += blockDim.x) {
+            int c = 0;
+            for (int j = 0; j < nb; ++j) c += pcnt[(int64_t)j * P + p];
+            cnt_p[p] = c;
+        }
+        if (tid == 0) {
+            int64_t nerr = 0;
+            for (int j = 0; j < nb; ++j) nerr += inv[j];
+            hdr->num_invalid = nerr;
+        }
+    }
+
+    ChunkData first;
+    if (wave < nchunk) first = load_chunk<FP8>(x, H, t, wave, s_scale);
+    scatter_token<FP8>(x, H, K, t, drow, first, recv_x, recv_scales, s_scale, nchunk);
+}
+
 // Decode dispatch into fixed-capacity receive rows, in one launch (expert e
 // owns rows [e*C, (e+1)*C); a slot whose rank in its expert reaches C is
 // dropped).  No row number depends on another expert's count, so nothing has
@@ -361,6 +448,51 @@ hipError_t launch_ll_dispatch(const uint16_t* x, const int64_t* idx, int T, int 
         hipLaunchKernelGGL(ll_dispatch_kernel<false>, dim3(grid), dim3(64 * nw), lds, s, x, idx,
                            T, H, K, E, C, cnt_e, recv_x, recv_scales, recv_src, dst_row,
                            num_invalid, nchunk);
+    return hipGetLastError();
+}
+
+hipError_t launch_layout_dispatch(const uint16_t* x, const int64_t* idx, int T, int H, int K,
+                                  int E, int P, bool fp8, void* ws, const WsMap& m,
+                                  int32_t* cnt_e, int32_t* cnt_p, uint8_t* in_part,
+                                  int32_t* off_e, int32_t* off_p, void* recv_x,
+                                  float* recv_scales, int32_t* recv_src, int32_t* dst_row,
+                                  hipStream_t s) {
+    const int nchunk = (H + kDispatchChunk - 1) / kDispatchChunk;
+    const int nw = nchunk < kDispatchMaxThreads / 64 ? nchunk : kDispatchMaxThreads / 64;
+    // The finishing sums are one round of loads per token workgroup and a
+    // bounded amount of work for workgroup 0; other shapes (and those with a
+    // single-launch layout) take the layout and the plain dispatch.
+    int seg_log2 = 0;                    // segment of 2^seg_log2 >= nb lanes per slot
+    while ((1 << seg_log2) < m.nb) ++seg_log2;
+    const bool fused = T > 0 && !layout_single_launch(T, K, E, P, m) && seg_log2 <= 6 &&
+                       ((int64_t)(K + 1) << seg_log2) <= 64 * nw &&
+                       (int64_t)(E + 1) * m.nb <= kLayoutDispatchMaxTerms;
+    if (!fused) {
+        hipError_t e = launch_layout(idx, T, K, E, P, ws, m, cnt_e, cnt_p, in_part, off_e, off_p,
+                                     s);
+        if (e != hipSuccess) return e;
+        return launch_dispatch(x, T, H, K, fp8, recv_x, recv_scales, recv_src, dst_row, ws, m, s);
+    }
+    hipError_t e = launch_layout_count(idx, T, K, E, P, ws, m, in_part, true, s);
+    if (e != hipSuccess) return e;
+    char* base = static_cast<char*>(ws);
+    WsHeader* hdr = reinterpret_cast<WsHeader*>(base);
+    const int* cnt = reinterpret_cast<const int*>(base + m.cnt_off);
+    const int* pcnt = reinterpret_cast<const int*>(base + m.pcnt_off);
+    const int* inv = reinterpret_cast<const int*>(base + m.inv_off);
+    const int* pre = reinterpret_cast<const int*>(base + m.pre_off);
+    const int* rows = reinterpret_cast<const int*>(base + m.rows_off);
+    const size_t lds = fp8 ? sizeof(float) * (size_t)(H / 128) : 0;
+    if (fp8)
+        hipLaunchKernelGGL(layout_dispatch_kernel<true>, dim3(T), dim3(64 * nw), lds, s, x, H, K,
+                           E, P, E / P, m.tb, m.nb, seg_log2, cnt, pre, pcnt, inv, rows, hdr,
+                           cnt_e, cnt_p, off_e, off_p, recv_x, recv_scales, recv_src, dst_row,
+                           nchunk);
+    else
+        hipLaunchKernelGGL(layout_dispatch_kernel<false>, dim3(T), dim3(64 * nw), lds, s, x, H, K,
+                           E, P, E / P, m.tb, m.nb, seg_log2, cnt, pre, pcnt, inv, rows, hdr,
+                           cnt_e, cnt_p, off_e, off_p, recv_x, recv_scales, recv_src, dst_row,
+                           nchunk);
     return hipGetLastError();
 }
 

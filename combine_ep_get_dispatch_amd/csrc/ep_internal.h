@@ -21,6 +21,10 @@ constexpr size_t kFusedLdsLimit = 156 * 1024;
 // ... and only for inputs of at most this many token blocks.
 constexpr int kFusedMaxBlocks = 2;
 
+// Packed slot after the count launch: (expert << kRankBits) | rank in block.
+constexpr int kRankBits = 12;     // rank inside a block < kLayoutEntries = 2^11
+static_assert(kLayoutEntries <= (1 << kRankBits), "rank field too narrow");
+
 __host__ __device__ inline int layout_tokens_per_block(int K) {
     int tb = kLayoutEntries / K;
     return tb < 1 ? 1 : tb;
@@ -40,13 +44,16 @@ static_assert(sizeof(WsHeader) <= kWsHeaderBytes, "header too large");
 //   cnt  int32 [nb][E] per-block expert counts
 //   pcnt int32 [nb][P] per-block distinct-token counts per partition
 //   inv  int32 [nb]    per-block invalid-slot counts
+//   pre  int32 [nb][E+1] per-block exclusive prefix of the expert counts over
+//                      the experts, pre[b][E] = the block's valid slots
+//                      (written only by the single-call layout + dispatch)
 //   rows int32 [T*K]   receive row of every slot (-1 if masked/invalid); the
 //                      count kernel leaves (expert << 12 | rank in block)
 //                      there and the finalize kernel turns it into the row
 struct WsMap {
     int nb = 0;        // token blocks
     int tb = 1;        // tokens per block
-    size_t cnt_off = 0, pcnt_off = 0, inv_off = 0, rows_off = 0, total = 0;
+    size_t cnt_off = 0, pcnt_off = 0, inv_off = 0, pre_off = 0, rows_off = 0, total = 0;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -58,7 +65,8 @@ inline WsMap ws_map(int T, int K, int E, int P) {
     m.cnt_off = kWsHeaderBytes;
     m.pcnt_off = m.cnt_off + align256(sizeof(int32_t) * (size_t)E * (size_t)m.nb);
     m.inv_off = m.pcnt_off + align256(sizeof(int32_t) * (size_t)P * (size_t)m.nb);
-    m.rows_off = m.inv_off + align256(sizeof(int32_t) * (size_t)m.nb);
+    m.pre_off = m.inv_off + align256(sizeof(int32_t) * (size_t)m.nb);
+    m.rows_off = m.pre_off + align256(sizeof(int32_t) * (size_t)(E + 1) * (size_t)m.nb);
     m.total = m.rows_off + align256(sizeof(int32_t) * (size_t)T * (size_t)K);
     return m;
 }
@@ -71,6 +79,15 @@ hipError_t launch_layout(const int64_t* idx, int T, int K, int E, int P, void* w
                          const WsMap& m, int32_t* cnt_e, int32_t* cnt_p, uint8_t* in_part,
                          int32_t* off_e, int32_t* off_p, hipStream_t s);
 
+// True when launch_layout takes its single-launch form for this shape.
+bool layout_single_launch(int T, int K, int E, int P, const WsMap& m);
+
+// The first of the two layout launches alone (T > 0): per-block counts,
+// partition rows and counts, invalid counts, packed (expert << 12 | rank)
+// slots, and with `with_pre` the per-block prefix matrix.
+hipError_t launch_layout_count(const int64_t* idx, int T, int K, int E, int P, void* ws,
+                               const WsMap& m, uint8_t* in_part, bool with_pre, hipStream_t s);
+
 // ---------------------------------------------------------------- dispatch --
 // One workgroup per token, one wave per 1024-channel chunk (16 channels per
 // lane), at most 16 waves; wider rows loop over their chunks.
@@ -80,6 +97,24 @@ constexpr int kDispatchChunk = 1024;
 hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K, bool fp8, void* recv_x,
                            float* recv_scales, int32_t* recv_src, int32_t* dst_row,
                            const void* ws, const WsMap& m, hipStream_t s);
+
+// Largest (E + 1) * blocks that workgroup 0 of the one-call layout + dispatch
+// sums (beyond it the call takes the two-step form).
+constexpr int64_t kLayoutDispatchMaxTerms = 32768;
+
+// Layout and dispatch in one call: the count launch (with the prefix matrix),
+// then one dispatch launch whose workgroups finish the layout themselves --
+// each token's rows from sums over the blocks, workgroup 0 the counts,
+// offsets and header.  Shapes with a single-launch layout run that layout and
+// the ordinary dispatch instead.  Same outputs as launch_layout followed by
+// launch_dispatch, except that the workspace's per-slot rows are left in
+// their packed form.
+hipError_t launch_layout_dispatch(const uint16_t* x, const int64_t* idx, int T, int H, int K,
+                                  int E, int P, bool fp8, void* ws, const WsMap& m,
+                                  int32_t* cnt_e, int32_t* cnt_p, uint8_t* in_part,
+                                  int32_t* off_e, int32_t* off_p, void* recv_x,
+                                  float* recv_scales, int32_t* recv_src, int32_t* dst_row,
+                                  hipStream_t s);
 
 // Fixed-capacity (decode) dispatch: one launch, one workgroup per token (T = 0
 // takes a small fill kernel instead) of kLlWaves waves, so that the routing scan every

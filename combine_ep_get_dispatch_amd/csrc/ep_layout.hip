@@ -38,8 +38,6 @@
 namespace ep {
 namespace {
 
-constexpr int kRankBits = 12;     // rank inside a block < kLayoutEntries = 2^11
-static_assert(kLayoutEntries <= (1 << kRankBits), "rank field too narrow");
 
 // Stored form of an expert id: the id itself, -1 for a masked slot, -2 for an
 // invalid one.
@@ -276,16 +274,23 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_fused_kernel(
 
 // ------------------------------------------------------------ two launches --
 
+// PRE: also write pre[b][0..E] = the block's exclusive prefix of its expert
+// counts over the experts (pre[b][E] = the block's valid slots), so that a
+// later kernel can form any expert offset as a sum over blocks instead of a
+// scan over experts (the single-call layout + dispatch uses this).
+template <bool PRE>
 __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
     const int64_t* __restrict__ idx, int T, int K, int E, int P, uint64_t pmagic, int TB,
     int ebits,
     int* __restrict__ cnt, int* __restrict__ pcnt, int* __restrict__ inv,
-    int* __restrict__ rows, uint8_t* __restrict__ in_part, int vec_rows) {
+    int* __restrict__ rows, uint8_t* __restrict__ in_part, int vec_rows,
+    int* __restrict__ pre) {
     extern __shared__ int smem[];
     int* wcnt = smem;                              // [waves][E]
     int* ids = wcnt + kLayoutWaves * E;            // [kLayoutEntries] stored ids
     int* rnk = ids + kLayoutEntries;               // [kLayoutEntries]
     int* pc = rnk + kLayoutEntries;                // [P]
+    int* bc = pc + P;                              // [E] block counts (PRE)
     __shared__ int s_err;
 
     const int tid = threadIdx.x;
@@ -319,7 +324,41 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
     __syncthreads();
     if (nerr) atomicAdd(&s_err, nerr);
 
-    rank_entries(ids, n, E, ebits, wcnt, rnk, cnt + (int64_t)b * E);
+    if constexpr (PRE) {
+        rank_entries(ids, n, E, ebits, wcnt, rnk, bc);   // ends with a barrier
+        if (tid < 64) {
+            // Wave 0 alone scans the block counts (lane l owns experts
+            // [l*per, l*per + per)); the other waves go on with the rows.
+            const int lane = tid;
+            const int per = (E + 63) >> 6;
+            const int e0 = lane * per;
+            int local = 0;
+            for (int i = 0; i < per; ++i) {
+                const int e = e0 + i;
+                if (e < E) {
+                    const int c = bc[e];
+                    cnt[(int64_t)b * E + e] = c;
+                    local += c;
+                }
+            }
+            int inc = local;
+            for (int d = 1; d < 64; d <<= 1) {
+                const int up = __shfl_up(inc, d);
+                if (lane >= d) inc += up;
+            }
+            int run = inc - local;
+            for (int i = 0; i < per; ++i) {
+                const int e = e0 + i;
+                if (e < E) {
+                    pre[(int64_t)b * (E + 1) + e] = run;
+                    run += bc[e];
+                }
+            }
+            if (lane == 63) pre[(int64_t)b * (E + 1) + E] = inc;
+        }
+    } else {
+        rank_entries(ids, n, E, ebits, wcnt, rnk, cnt + (int64_t)b * E);
+    }
     for (int j = tid; j < n; j += kLayoutThreads) {
         const int e = ids[j];
         rows[(int64_t)t0 * K + j] = (e >= 0) ? (e << kRankBits) | rnk[j] : -1;
@@ -414,6 +453,52 @@ size_t layout_fused_lds_bytes(int T, int K, int E, int P) {
     return sizeof(int) * ((size_t)(4 + kLayoutWaves) * E + kLayoutEntries + P) + ids;
 }
 
+bool layout_single_launch(int T, int K, int E, int P, const WsMap& m) {
+    return T > 0 && m.nb <= kFusedMaxBlocks && layout_fused_lds_bytes(T, K, E, P) <= kFusedLdsLimit;
+}
+
+namespace {
+
+int expert_bits(int E) {
+    int ebits = 0;
+    while ((1 << ebits) < E) ++ebits;
+    return ebits;
+}
+
+uint64_t partition_magic(int Ep) {   // ceil(2^32 / Ep)
+    return ((uint64_t)1 << 32) / (uint64_t)Ep + ((((uint64_t)1 << 32) % (uint64_t)Ep) ? 1 : 0);
+}
+
+bool vector_rows(int P, const uint8_t* in_part) {
+    return (P % 16 == 0) && (reinterpret_cast<uintptr_t>(in_part) % 16 == 0);
+}
+
+}  // namespace
+
+hipError_t launch_layout_count(const int64_t* idx, int T, int K, int E, int P, void* ws,
+                               const WsMap& m, uint8_t* in_part, bool with_pre, hipStream_t s) {
+    char* base = static_cast<char*>(ws);
+    int* cnt = reinterpret_cast<int*>(base + m.cnt_off);
+    int* pcnt = reinterpret_cast<int*>(base + m.pcnt_off);
+    int* inv = reinterpret_cast<int*>(base + m.inv_off);
+    int* pre = reinterpret_cast<int*>(base + m.pre_off);
+    int* rows = reinterpret_cast<int*>(base + m.rows_off);
+    const int ebits = expert_bits(E);
+    const uint64_t pmagic = partition_magic(E / P);
+    const int vec = vector_rows(P, in_part);
+    const size_t lds = sizeof(int) * ((size_t)kLayoutWaves * E + 2 * kLayoutEntries + P +
+                                      (with_pre ? (size_t)E : 0));
+    if (with_pre)
+        hipLaunchKernelGGL(layout_count_kernel<true>, dim3(m.nb), dim3(kLayoutThreads), lds, s,
+                           idx, T, K, E, P, pmagic, m.tb, ebits, cnt, pcnt, inv, rows, in_part,
+                           vec, pre);
+    else
+        hipLaunchKernelGGL(layout_count_kernel<false>, dim3(m.nb), dim3(kLayoutThreads), lds, s,
+                           idx, T, K, E, P, pmagic, m.tb, ebits, cnt, pcnt, inv, rows, in_part,
+                           vec, pre);
+    return hipGetLastError();
+}
+
 hipError_t launch_layout(const int64_t* idx, int T, int K, int E, int P, void* ws,
                          const WsMap& m, int32_t* cnt_e, int32_t* cnt_p, uint8_t* in_part,
                          int32_t* off_e, int32_t* off_p, hipStream_t s) {
@@ -424,23 +509,21 @@ hipError_t launch_layout(const int64_t* idx, int T, int K, int E, int P, void* w
                            cnt_p, off_e, off_p);
         return hipGetLastError();
     }
-    int ebits = 0;
-    while ((1 << ebits) < E) ++ebits;
+    const int ebits = expert_bits(E);
     const int Ep = E / P;
-    const uint64_t pmagic = ((uint64_t)1 << 32) / (uint64_t)Ep +
-                            ((((uint64_t)1 << 32) % (uint64_t)Ep) ? 1 : 0);   // ceil(2^32/Ep)
+    const uint64_t pmagic = partition_magic(Ep);
     int* rows = reinterpret_cast<int*>(base + m.rows_off);
-    const int vec_rows = (P % 16 == 0) && (reinterpret_cast<uintptr_t>(in_part) % 16 == 0);
+    const int vec_rows = vector_rows(P, in_part);
 
     const size_t fused_lds = layout_fused_lds_bytes(T, K, E, P);
-    if (m.nb <= kFusedMaxBlocks && fused_lds <= kFusedLdsLimit) {
-        static bool attr_set = false;   // raise the dynamic-LDS cap once per process
-        if (!attr_set) {
+    if (layout_single_launch(T, K, E, P, m)) {
+        if (fused_lds > 64 * 1024) {
+            // Raise the dynamic-LDS cap (per device, so on every call: it is a
+            // host-side attribute update).
             hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(layout_fused_kernel),
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                                (int)kFusedLdsLimit);
             if (e != hipSuccess) return e;
-            attr_set = true;
         }
         hipLaunchKernelGGL(layout_fused_kernel, dim3(m.nb), dim3(kLayoutThreads), fused_lds, s,
                            idx, T, K, E, P, Ep, pmagic, m.tb, ebits, rows, in_part, vec_rows, hdr,
@@ -448,14 +531,11 @@ hipError_t launch_layout(const int64_t* idx, int T, int K, int E, int P, void* w
         return hipGetLastError();
     }
 
+    hipError_t err = launch_layout_count(idx, T, K, E, P, ws, m, in_part, false, s);
+    if (err != hipSuccess) return err;
     int* cnt = reinterpret_cast<int*>(base + m.cnt_off);
     int* pcnt = reinterpret_cast<int*>(base + m.pcnt_off);
     int* inv = reinterpret_cast<int*>(base + m.inv_off);
-    const size_t lds1 = sizeof(int) * ((size_t)kLayoutWaves * E + 2 * kLayoutEntries + P);
-    hipLaunchKernelGGL(layout_count_kernel, dim3(m.nb), dim3(kLayoutThreads), lds1, s, idx, T, K,
-                       E, P, pmagic, m.tb, ebits, cnt, pcnt, inv, rows, in_part, vec_rows);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
     const size_t lds2 = sizeof(int) * 3 * (size_t)E;
     hipLaunchKernelGGL(layout_finalize_kernel, dim3(m.nb), dim3(kLayoutThreads), lds2, s, T, K, E,
                        P, E / P, m.tb, m.nb, cnt, pcnt, inv, rows, hdr, cnt_e, cnt_p, off_e,

@@ -130,6 +130,25 @@ ep_status_t ep_dispatch(const void *x, int32_t num_tokens, int32_t hidden,
                         void *stream);
 
 /*
+ * Layout and dispatch in one call: exactly the outputs of
+ * ep_get_dispatch_layout followed by ep_dispatch with the same arguments
+ * (every argument has the meaning given there), computed with one kernel
+ * launch fewer -- the dispatch kernel finishes the layout itself, so the
+ * counts, offsets and the header are written by the same launch that moves
+ * the rows.  The workspace afterwards serves ep_get_device_error, but not a
+ * later ep_dispatch (its per-slot rows are left in an intermediate form).
+ */
+ep_status_t ep_layout_dispatch(const void *x, int32_t num_tokens, int32_t hidden,
+                               const int64_t *topk_idx, int32_t num_topk, int32_t num_experts,
+                               int32_t num_partitions, ep_dtype_t out_dtype,
+                               int32_t *num_tokens_per_expert,
+                               int32_t *num_tokens_per_partition,
+                               uint8_t *is_token_in_partition, int32_t *expert_offsets,
+                               int32_t *partition_offsets, void *recv_x, float *recv_scales,
+                               int32_t *recv_src_token, int32_t *dst_row, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
  * Combine (the "combine" half of "DeepEP: Optimizing MoE Communication"):
  * bring each token's expert outputs back and reduce them with its gate
  * weights.  For every token t and channel h:

@@ -42,12 +42,16 @@ def ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.abs(m(a) - m(b))
 
 
-def run_gpu(case, with_combine=True, workspace=None):
-    """The whole path on cuda:0; returns numpy copies of every output."""
+def run_gpu(case, with_combine=True, workspace=None, one_call=False):
+    """The whole path on cuda:0 (layout and dispatch as two calls, or as the
+    one ep_layout_dispatch call); returns numpy copies of every output."""
     idx = torch.from_numpy(case.topk_idx).cuda()
     x = to_dev_bf16(case.x_bits)
-    lay = ep.get_dispatch_layout(idx, case.E, case.P, workspace=workspace)
-    d = ep.dispatch(x, idx, case.E, case.P, lay.workspace, fp8=case.fp8)
+    if one_call:
+        lay, d = ep.layout_dispatch(x, idx, case.E, case.P, workspace=workspace, fp8=case.fp8)
+    else:
+        lay = ep.get_dispatch_layout(idx, case.E, case.P, workspace=workspace)
+        d = ep.dispatch(x, idx, case.E, case.P, lay.workspace, fp8=case.fp8)
     res = dict(
         num_tokens_per_expert=lay.num_tokens_per_expert.cpu().numpy(),
         num_tokens_per_partition=lay.num_tokens_per_partition.cpu().numpy(),
@@ -97,15 +101,16 @@ def compare(g: dict, o: dict, case, with_combine=True) -> dict:
     return stats
 
 
-def check_case(case, with_combine=True, label=""):
-    announce("%s T=%d H=%d E=%d P=%d K=%d fp8=%s" % (label or case.name, case.T, case.H, case.E,
+def check_case(case, with_combine=True, label="", one_call=False):
+    label = (label or case.name) + (" (one call)" if one_call else "")
+    announce("%s T=%d H=%d E=%d P=%d K=%d fp8=%s" % (label, case.T, case.H, case.E,
                                                      case.P, case.K, case.fp8))
     t0 = time.time()
-    g = run_gpu(case, with_combine)
+    g = run_gpu(case, with_combine, one_call=one_call)
     t1 = time.time()
     o = run_oracle(case, with_combine)
     t2 = time.time()
     stats = compare(g, o, case, with_combine)
     stats.update(gpu_s=round(t1 - t0, 2), oracle_s=round(t2 - t1, 2))
-    announce("%s ok %s" % (label or case.name, stats))
+    announce("%s ok %s" % (label, stats))
     return stats

@@ -21,10 +21,11 @@ from parity import announce, check_case, run_gpu
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("one_call", [False, True], ids=["two_calls", "one_call"])
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skewed", "coarse"])
-def test_configuration_full_size(name):
+def test_configuration_full_size(name, one_call):
     case = wl.make(name)
-    stats = check_case(case, label="config " + name)
+    stats = check_case(case, label="config " + name, one_call=one_call)
     assert stats["N"] == case.T * case.K
 
 
@@ -57,18 +58,21 @@ GENERIC = [
 def test_generic_case(T, H, E, P, K, seed, kw):
     case = wl.random_case(T, H, E, P, K, seed, **kw)
     check_case(case, label="random seed=%d" % seed)
+    check_case(case, label="random seed=%d" % seed, one_call=True)
 
 
-def test_all_tokens_to_one_expert():
-    case = wl.random_case(3000, 256, 32, 8, 1, 21)
+@pytest.mark.parametrize("one_call", [False, True], ids=["two_calls", "one_call"])
+def test_all_tokens_to_one_expert(one_call):
+    case = wl.random_case(5000, 256, 32, 8, 1, 21)     # 3 token blocks
     case.topk_idx[:] = 17
-    check_case(case, label="one hot expert")
+    check_case(case, label="one hot expert", one_call=one_call)
 
 
-def test_every_slot_masked():
-    case = wl.random_case(300, 256, 16, 4, 4, 22)
+@pytest.mark.parametrize("one_call", [False, True], ids=["two_calls", "one_call"])
+def test_every_slot_masked(one_call):
+    case = wl.random_case(3000, 256, 16, 4, 4, 22)
     case.topk_idx[:] = -1
-    stats = check_case(case, label="all masked")
+    stats = check_case(case, label="all masked", one_call=one_call)
     assert stats["N"] == 0
 
 
@@ -79,6 +83,8 @@ def test_invalid_ids_are_counted():
     g = run_gpu(case)
     assert g["num_invalid"] == n_bad
     check_case(case, label="invalid ids")
+    assert run_gpu(case, one_call=True)["num_invalid"] == n_bad
+    check_case(case, label="invalid ids", one_call=True)
 
 
 def test_zero_tokens():
@@ -95,6 +101,12 @@ def test_zero_tokens():
     assert lay.partition_offsets.cpu().tolist() == [0] * 5
     assert lay.num_tokens_per_expert.sum().item() == 0
     assert ep.get_device_error(lay.workspace) == 0
+    lay1, d1 = ep.layout_dispatch(x, idx, 16, 4, fp8=True)
+    torch.cuda.synchronize()
+    assert lay1.expert_offsets.cpu().tolist() == [0] * 17
+    assert lay1.partition_offsets.cpu().tolist() == [0] * 5
+    assert lay1.num_tokens_per_partition.sum().item() == 0
+    assert ep.get_device_error(lay1.workspace) == 0
 
 
 def test_workspace_reuse_across_shapes():
@@ -104,9 +116,10 @@ def test_workspace_reuse_across_shapes():
     small = wl.random_case(37, 512, 16, 4, 2, 32, fp8=True)
     ws = ep.new_workspace(5000, 8, 64, 16)
     from parity import compare, run_oracle
-    for case in [big, small, small, big]:
-        announce("workspace reuse T=%d" % case.T)
-        g = run_gpu(case, workspace=ws)
+    for case, one_call in [(big, False), (small, False), (small, True), (big, True),
+                           (big, False), (small, True)]:
+        announce("workspace reuse T=%d one_call=%s" % (case.T, one_call))
+        g = run_gpu(case, workspace=ws, one_call=one_call)
         compare(g, run_oracle(case), case)
 
 
