@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void layout_dispatch_kernel(
     WsHeader* __restrict__ hdr, int32_t* __restrict__ cnt_e, int32_t* __restrict__ cnt_p,
     int32_t* __restrict__ off_e, int32_t* __restrict__ off_p, void* __restrict__ recv_x,
     float* __restrict__ recv_scales, int32_t* __restrict__ recv_src,
-    int32_t* __restrict__ dst_row, int nchunk) {
+    int32_t* __restrict__ dst_row, int nchunk, int nrows) {
     extern __shared__ float s_scale[];   // [G] scales of this token (FP8)
     __shared__ int s_row[64];            // receive row of slot k (K <= 64)
     __shared__ int s_n;                  // N
@@ -236,8 +236,13 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void layout_dispatch_kernel(
         }
         for (int o = S >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o);
         if (j == 0) {
-            if (k < K) s_row[k] = pk >= 0 ? v + (pk & ((1 << kRankBits) - 1)) : -1;
-            else if (k == K) s_n = v;
+            if (k < K) {
+                int r = pk >= 0 ? v + (pk & ((1 << kRankBits) - 1)) : -1;
+                if (r >= nrows) r = -1;    // only with a workspace from another layout
+                s_row[k] = r;
+            } else if (k == K) {
+                s_n = v;
+            }
         }
     }
     __syncthreads();
@@ -487,12 +492,12 @@ hipError_t launch_layout_dispatch(const uint16_t* x, const int64_t* idx, int T, 
         hipLaunchKernelGGL(layout_dispatch_kernel<true>, dim3(T), dim3(64 * nw), lds, s, x, H, K,
                            E, P, E / P, m.tb, m.nb, seg_log2, cnt, pre, pcnt, inv, rows, hdr,
                            cnt_e, cnt_p, off_e, off_p, recv_x, recv_scales, recv_src, dst_row,
-                           nchunk);
+                           nchunk, T * K);
     else
         hipLaunchKernelGGL(layout_dispatch_kernel<false>, dim3(T), dim3(64 * nw), lds, s, x, H, K,
                            E, P, E / P, m.tb, m.nb, seg_log2, cnt, pre, pcnt, inv, rows, hdr,
                            cnt_e, cnt_p, off_e, off_p, recv_x, recv_scales, recv_src, dst_row,
-                           nchunk);
+                           nchunk, T * K);
     return hipGetLastError();
 }
 

@@ -87,9 +87,21 @@ __device__ int block_exclusive_scan(int* a, int n, int* red) {
 // call rnk[j] is the number of entries before j (inside the workgroup) with
 // the same expert, -1 for entries without one; if blk_cnt is given,
 // blk_cnt[e] receives the workgroup's count of expert e.
+//
+// The lanes of a 64-entry chunk that hold the same expert (the "match" mask)
+// come either from one ballot per id bit (ebits ballots, each a handful of
+// VALU instructions per lane) or, when mtab is given ([kLayoutWaves][E][2]
+// zeroed 32-bit LDS words, for E <= kMatchTableMaxE), from the wave's own
+// table: every lane ORs its bit into mtab[e] (lanes 0-31 the first word,
+// 32-63 the second), reads both words back and clears them -- one wave's LDS
+// operations complete in issue order, so the reads see the whole chunk's
+// bits and the clears follow every read.  (32-bit words, so that only 4-byte
+// alignment is needed: the dynamic LDS need not start 8-byte aligned.)  The
+// table costs a few LDS operations per chunk instead of the ballots' VALU
+// work, which is what bounds this loop on the few workgroups a layout uses.
 template <typename Id>
 __device__ void rank_entries(const Id* ids, int n, int E, int ebits, int* wcnt, int* rnk,
-                             int* blk_cnt) {
+                             int* blk_cnt, unsigned* mtab = nullptr) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nchunks = (n + 63) >> 6;
@@ -97,16 +109,32 @@ __device__ void rank_entries(const Id* ids, int n, int E, int ebits, int* wcnt, 
     const int c0 = wave * per;
     const int c1 = min(c0 + per, nchunks);
     int* myw = wcnt + wave * E;
+    unsigned* myt = mtab ? mtab + (size_t)wave * 2 * E : nullptr;
     for (int c = c0; c < c1; ++c) {          // wave-uniform loop: ballots are safe
         const int j = (c << 6) + lane;
         const int e0 = (j < n) ? (int)ids[j] : -1;
         const bool valid = e0 >= 0;
         const int e = valid ? e0 : 0;
-        uint64_t m = __ballot(valid);
-        for (int bit = 0; bit < ebits; ++bit) {
-            const bool on = (e >> bit) & 1;
-            const uint64_t bb = __ballot(on);
-            m &= on ? bb : ~bb;
+        uint64_t m;
+        if (myt) {
+            unsigned* w = myt + 2 * e;
+            if (valid) __hip_atomic_fetch_or(w + (lane >> 5), 1u << (lane & 31), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_WAVEFRONT);
+            unsigned lo = 0, hi = 0;
+            if (valid) {
+                lo = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+                hi = __hip_atomic_load(w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+                __hip_atomic_store(w, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+                __hip_atomic_store(w + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+            }
+            m = ((uint64_t)hi << 32) | lo;
+        } else {
+            m = __ballot(valid);
+            for (int bit = 0; bit < ebits; ++bit) {
+                const bool on = (e >> bit) & 1;
+                const uint64_t bb = __ballot(on);
+                m &= on ? bb : ~bb;
+            }
         }
         if (valid) {
             rnk[j] = myw[e] + __popcll(m & ((1ull << lane) - 1ull));
@@ -131,6 +159,72 @@ __device__ void rank_entries(const Id* ids, int n, int E, int ebits, int* wcnt, 
         if (e >= 0) rnk[j] += wcnt[((j >> 6) / per) * E + e];
     }
     __syncthreads();
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (row
+// shifts by 1, 2, 4, 8 inside each 16-lane row, then the row broadcasts of
+// lanes 15 and 31); no LDS traffic.  Lanes a move has no source for take 0.
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+    const int lane = threadIdx.x & 63;
+    int t;
+    t = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    if ((lane & 15) >= 1) x += t;
+    t = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    if ((lane & 15) >= 2) x += t;
+    t = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    if ((lane & 15) >= 4) x += t;
+    t = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    if ((lane & 15) >= 8) x += t;
+    t = __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
+    if (lane & 16) x += t;
+    t = __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
+    if (lane & 32) x += t;
+    return x;
+}
+
+// One wave writes the block's expert counts cnt[0..E) and their exclusive
+// prefix pre[0..E] (pre[E] = total) from bc, which holds 64*PER ints (zero
+// past E); lane l owns experts [l*PER, l*PER + PER).
+template <int PER>
+__device__ void scan_block_counts(const int* bc, int E, int* cnt, int* pre) {
+    const int lane = threadIdx.x & 63;
+    const int e0 = lane * PER;
+    int v[PER];
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        v[i] = bc[e0 + i];
+        local += v[i];
+    }
+    const int inc = wave_inclusive_sum(local);
+    int run = inc - local;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        if (e0 + i < E) {
+            cnt[e0 + i] = v[i];
+            pre[e0 + i] = run;
+        }
+        run += v[i];
+    }
+    if (lane == 63) pre[E] = inc;
+}
+
+// Per-lane share of experts for scan_block_counts: ceil(E / 64) rounded up to
+// a power of two (<= 16 for E <= 1024).
+__host__ __device__ inline int scan_per(int E) {
+    int per = 1;
+    while (per * 64 < E) per <<= 1;
+    return per;
+}
+
+// Match tables are used up to this many experts ([waves][E][2] 32-bit words).
+constexpr int kMatchTableMaxE = 256;
+
+// layout_count_kernel's dynamic LDS, in ints: wcnt [waves][E], ids and rnk
+// [kLayoutEntries] each, pc [P], with PRE bc [64 * scan_per(E)]; the match
+// tables follow at the returned offset.
+__host__ __device__ inline int count_table_offset(int E, int P, bool pre) {
+    return kLayoutWaves * E + 2 * kLayoutEntries + P + (pre ? 64 * scan_per(E) : 0);
 }
 
 // Partition of expert e: e / Ep computed as (e * ceil(2^32 / Ep)) >> 32,
@@ -290,7 +384,10 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
     int* ids = wcnt + kLayoutWaves * E;            // [kLayoutEntries] stored ids
     int* rnk = ids + kLayoutEntries;               // [kLayoutEntries]
     int* pc = rnk + kLayoutEntries;                // [P]
-    int* bc = pc + P;                              // [E] block counts (PRE)
+    int* bc = pc + P;                              // [64 * scan_per(E)] block counts (PRE)
+    // [waves][E][2] match tables (E <= kMatchTableMaxE)
+    unsigned* mtab = reinterpret_cast<unsigned*>(smem + count_table_offset(E, P, PRE));
+    const bool use_mtab = E <= kMatchTableMaxE;
     __shared__ int s_err;
 
     const int tid = threadIdx.x;
@@ -310,6 +407,10 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
     }
     for (int i = tid; i < kLayoutWaves * E; i += kLayoutThreads) wcnt[i] = 0;
     for (int i = tid; i < P; i += kLayoutThreads) pc[i] = 0;
+    if (PRE)
+        for (int i = E + tid; i < 64 * scan_per(E); i += kLayoutThreads) bc[i] = 0;
+    if (use_mtab)
+        for (int i = tid; i < 2 * kLayoutWaves * E; i += kLayoutThreads) mtab[i] = 0u;
     if (tid == 0) s_err = 0;
     int nerr = 0;
 #pragma unroll
@@ -324,40 +425,24 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
     __syncthreads();
     if (nerr) atomicAdd(&s_err, nerr);
 
+    unsigned* tab = use_mtab ? mtab : nullptr;
     if constexpr (PRE) {
-        rank_entries(ids, n, E, ebits, wcnt, rnk, bc);   // ends with a barrier
+        rank_entries(ids, n, E, ebits, wcnt, rnk, bc, tab);   // ends with a barrier
         if (tid < 64) {
-            // Wave 0 alone scans the block counts (lane l owns experts
-            // [l*per, l*per + per)); the other waves go on with the rows.
-            const int lane = tid;
-            const int per = (E + 63) >> 6;
-            const int e0 = lane * per;
-            int local = 0;
-            for (int i = 0; i < per; ++i) {
-                const int e = e0 + i;
-                if (e < E) {
-                    const int c = bc[e];
-                    cnt[(int64_t)b * E + e] = c;
-                    local += c;
-                }
+            // Wave 0 alone scans the block counts; the other waves go on
+            // with the rows.
+            int* cb = cnt + (int64_t)b * E;
+            int* pb = pre + (int64_t)b * (E + 1);
+            switch (scan_per(E)) {
+                case 1: scan_block_counts<1>(bc, E, cb, pb); break;
+                case 2: scan_block_counts<2>(bc, E, cb, pb); break;
+                case 4: scan_block_counts<4>(bc, E, cb, pb); break;
+                case 8: scan_block_counts<8>(bc, E, cb, pb); break;
+                default: scan_block_counts<16>(bc, E, cb, pb); break;
             }
-            int inc = local;
-            for (int d = 1; d < 64; d <<= 1) {
-                const int up = __shfl_up(inc, d);
-                if (lane >= d) inc += up;
-            }
-            int run = inc - local;
-            for (int i = 0; i < per; ++i) {
-                const int e = e0 + i;
-                if (e < E) {
-                    pre[(int64_t)b * (E + 1) + e] = run;
-                    run += bc[e];
-                }
-            }
-            if (lane == 63) pre[(int64_t)b * (E + 1) + E] = inc;
         }
     } else {
-        rank_entries(ids, n, E, ebits, wcnt, rnk, cnt + (int64_t)b * E);
+        rank_entries(ids, n, E, ebits, wcnt, rnk, cnt + (int64_t)b * E, tab);
     }
     for (int j = tid; j < n; j += kLayoutThreads) {
         const int e = ids[j];
@@ -475,6 +560,13 @@ bool vector_rows(int P, const uint8_t* in_part) {
 
 }  // namespace
 
+// Dynamic LDS of layout_count_kernel.
+size_t count_lds_bytes(int E, int P, bool with_pre) {
+    size_t bytes = sizeof(int) * (size_t)count_table_offset(E, P, with_pre);
+    if (E <= kMatchTableMaxE) bytes += sizeof(unsigned) * 2 * (size_t)kLayoutWaves * E;
+    return bytes;
+}
+
 hipError_t launch_layout_count(const int64_t* idx, int T, int K, int E, int P, void* ws,
                                const WsMap& m, uint8_t* in_part, bool with_pre, hipStream_t s) {
     char* base = static_cast<char*>(ws);
@@ -486,8 +578,7 @@ hipError_t launch_layout_count(const int64_t* idx, int T, int K, int E, int P, v
     const int ebits = expert_bits(E);
     const uint64_t pmagic = partition_magic(E / P);
     const int vec = vector_rows(P, in_part);
-    const size_t lds = sizeof(int) * ((size_t)kLayoutWaves * E + 2 * kLayoutEntries + P +
-                                      (with_pre ? (size_t)E : 0));
+    const size_t lds = count_lds_bytes(E, P, with_pre);
     if (with_pre)
         hipLaunchKernelGGL(layout_count_kernel<true>, dim3(m.nb), dim3(kLayoutThreads), lds, s,
                            idx, T, K, E, P, pmagic, m.tb, ebits, cnt, pcnt, inv, rows, in_part,
