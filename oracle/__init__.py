@@ -67,6 +67,9 @@ def _bind(lib):
     lib.oracle_ll_layout.restype = _i64
     lib.oracle_dispatch_rows_bf16.argtypes = [_u16p, _i32, _i32, _i32p, _i64, _u16p]
     lib.oracle_dispatch_rows_fp8.argtypes = [_u16p, _i32, _i32, _i32p, _i64, _u8p, _f32p]
+    lib.oracle_dedup_layout.argtypes = [_i64p, _i32, _i32, _i32, _i32, _i32p, _i32p, _i32p,
+                                        _i32p, _i32p, _i32p, _i32p]
+    lib.oracle_dedup_layout.restype = _i32
     return lib
 
 
@@ -261,6 +264,43 @@ def run_ll(topk_idx, x_bits, E, C, fp8, y_bits=None, topk_weights=None) -> dict:
         res["recv_x"] = dispatch_rows_bf16(x_bits, src)
     if y_bits is not None:
         res["out"] = combine(y_bits, res["dst_row"], topk_weights)
+    return res
+
+
+def dedup_layout(topk_idx: np.ndarray, E: int, P: int) -> dict:
+    """De-duplicated per-partition rows (see ``oracle_dedup_layout``), with
+    the offsets layout and permutation it builds on."""
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
+    T, K = idx.shape
+    lay = layout(idx, E, P)
+    dst, src = permutation(idx, E, lay["expert_offsets"])
+    Kp = min(K, P)
+    ptok_off = np.empty(P + 1, np.int32)
+    dd_row = np.empty((T, P), np.int32)
+    dd_src = np.empty(T * Kp, np.int32)
+    dd_idx = np.empty((T * Kp, K), np.int32)
+    slot_src = np.empty(T * K, np.int32)
+    cnt_p = np.ascontiguousarray(lay["num_tokens_per_partition"], dtype=np.int32)
+    n = _load().oracle_dedup_layout(_ptr(idx, ctypes.c_int64), T, K, E, P,
+                                    _ptr(cnt_p, ctypes.c_int32), _ptr(dst, ctypes.c_int32),
+                                    _ptr(ptok_off, ctypes.c_int32), _ptr(dd_row, ctypes.c_int32),
+                                    _ptr(dd_src, ctypes.c_int32), _ptr(dd_idx, ctypes.c_int32),
+                                    _ptr(slot_src, ctypes.c_int32))
+    res = dict(lay)
+    res.update(dst_row=dst, recv_src_token=src, partition_token_offsets=ptok_off,
+               dedup_row=dd_row, dedup_src_token=dd_src, dedup_topk_idx=dd_idx,
+               slot_src_row=slot_src, num_dedup_rows=int(n))
+    return res
+
+
+def run_dedup(topk_idx, x_bits, E, P, fp8) -> dict:
+    """The de-duplicated dispatch: layout, dedup rows and their data."""
+    res = dedup_layout(topk_idx, E, P)
+    src = res["dedup_src_token"]
+    if fp8:
+        res["dedup_x"], res["dedup_scales"] = dispatch_rows_fp8(x_bits, src)
+    else:
+        res["dedup_x"] = dispatch_rows_bf16(x_bits, src)
     return res
 
 

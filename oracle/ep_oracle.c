@@ -399,6 +399,90 @@ void oracle_dispatch_rows_fp8(const uint16_t *x, int32_t T, int32_t H,
 }
 
 /* ------------------------------------------------------------------------ */
+/* De-duplicated per-partition dispatch                                      */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * One copy of a token per destination partition instead of one per selected
+ * expert.  Group-limited gating keeps the number of partitions a token
+ * reaches small ("DeepSeek releases DeepEP ...", section "DeepEP: Optimizing
+ * MoE Communication"), and merging what goes to the same destination before
+ * it is sent is how the library saves link traffic ("DeepSeek Open Source
+ * Week: A carnival of technology inclusion ...", section 4).  The pages give
+ * no layout; this oracle takes the plainest one:
+ *   ptok_off [P+1]   exclusive prefix of the per-partition token counts
+ *                    (cnt_p of oracle_layout)
+ *   the rows of partition p are [ptok_off[p], ptok_off[p+1]), one per token
+ *   with a valid slot in p, in token order
+ *   dd_row   [T][P]  row of (t, p), -1 if t has no valid slot in p
+ *   dd_src   [RD]    source token of each row, -1 for rows >= ptok_off[P]
+ *                    (RD = T * min(K, P) rows, an upper bound)
+ *   dd_idx   [RD][K] for row (t, p): the local expert id e - p*(E/P) of each
+ *                    slot k of t whose expert is in p, else -1 (rows beyond
+ *                    ptok_off[P] are -1 throughout)
+ *   slot_src [T*K]   for every expert-major receive row r = dst[t][k] (as
+ *                    oracle_permutation numbers them): the row of (t, part of
+ *                    slot k), so an expert's inputs are dd rows
+ *                    slot_src[expert_offsets[e] .. expert_offsets[e+1]);
+ *                    -1 for r >= N
+ * Returns the number of rows, ptok_off[P].
+ */
+int32_t oracle_dedup_layout(const int64_t *idx, int32_t T, int32_t K, int32_t E, int32_t P,
+                            const int32_t *cnt_p, const int32_t *dst, int32_t *ptok_off,
+                            int32_t *dd_row, int32_t *dd_src, int32_t *dd_idx,
+                            int32_t *slot_src)
+{
+    int32_t Ep = E / P;
+    int32_t Kp = K < P ? K : P;
+    int64_t RD = (int64_t)T * Kp;
+    int32_t *next = (int32_t *)calloc((size_t)P + 1, sizeof(int32_t));
+    ptok_off[0] = 0;
+    for (int32_t p = 0; p < P; ++p)
+        ptok_off[p + 1] = ptok_off[p] + cnt_p[p];
+    for (int64_t i = 0; i < (int64_t)T * P; ++i)
+        dd_row[i] = -1;
+    for (int64_t r = 0; r < RD; ++r) {
+        dd_src[r] = -1;
+        for (int32_t k = 0; k < K; ++k)
+            dd_idx[r * K + k] = -1;
+    }
+    for (int32_t t = 0; t < T; ++t) {
+        for (int32_t p = 0; p < P; ++p) {
+            int member = 0;
+            for (int32_t k = 0; k < K; ++k) {
+                int64_t v = idx[(int64_t)t * K + k];
+                if (v >= 0 && v < E && v / Ep == p)
+                    member = 1;
+            }
+            if (!member)
+                continue;
+            int32_t r = ptok_off[p] + next[p];
+            next[p] += 1;
+            dd_row[(int64_t)t * P + p] = r;
+            dd_src[r] = t;
+            for (int32_t k = 0; k < K; ++k) {
+                int64_t v = idx[(int64_t)t * K + k];
+                if (v >= 0 && v < E && v / Ep == p)
+                    dd_idx[(int64_t)r * K + k] = (int32_t)(v - (int64_t)p * Ep);
+            }
+        }
+    }
+    for (int64_t r = 0; r < (int64_t)T * K; ++r)
+        slot_src[r] = -1;
+    for (int32_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t r = dst[(int64_t)t * K + k];
+            if (r < 0)
+                continue;
+            int64_t v = idx[(int64_t)t * K + k];
+            slot_src[r] = dd_row[(int64_t)t * P + v / Ep];
+        }
+    }
+    free(next);
+    return ptok_off[P];
+}
+
+/* ------------------------------------------------------------------------ */
 /* Combine                                                                   */
 /* ------------------------------------------------------------------------ */
 

@@ -219,3 +219,34 @@ def ll_rank_batch(idx_batch: np.ndarray, E: int) -> np.ndarray:
     same = (flat[:, :, None] == flat[:, None, :]) & valid[:, None, :]
     rank = (same & earlier[None]).sum(axis=2)
     return np.where(valid, rank, -1).reshape(B, T, K)
+
+
+def dedup_layout(idx: np.ndarray, E: int, P: int) -> dict:
+    """De-duplicated per-partition rows from the partition mask with cumsum:
+    a token's row in partition p is the partition's offset plus the number of
+    earlier member tokens (an exclusive running sum down the mask column)."""
+    idx = np.asarray(idx, np.int64)
+    T, K = idx.shape
+    Ep = E // P
+    Kp = min(K, P)
+    lay = layout(idx, E, P)
+    in_part = lay["is_token_in_partition"].astype(np.int64)
+    cnt_p = in_part.sum(axis=0)
+    ptok_off = np.concatenate([[0], np.cumsum(cnt_p)]).astype(np.int32)
+    before = np.cumsum(in_part, axis=0) - in_part          # earlier member tokens
+    dd_row = np.where(in_part == 1, ptok_off[:-1][None, :] + before, -1).astype(np.int32)
+    dd_src = np.full(T * Kp, -1, np.int32)
+    dd_idx = np.full((T * Kp, K), -1, np.int32)
+    tt, pp = np.nonzero(dd_row >= 0)
+    dd_src[dd_row[tt, pp]] = tt
+    valid = (idx >= 0) & (idx < E)
+    for t, p in zip(tt, pp):
+        r = dd_row[t, p]
+        local = valid[t] & (idx[t] // Ep == p)
+        dd_idx[r, local] = idx[t, local] - p * Ep
+    dst, _ = permutation(idx, E)
+    slot_src = np.full(T * K, -1, np.int32)
+    vt, vk = np.nonzero(valid)
+    slot_src[dst[vt, vk]] = dd_row[vt, idx[vt, vk] // Ep]
+    return dict(partition_token_offsets=ptok_off, dedup_row=dd_row, dedup_src_token=dd_src,
+                dedup_topk_idx=dd_idx, slot_src_row=slot_src, num_dedup_rows=int(ptok_off[-1]))

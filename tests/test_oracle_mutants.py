@@ -33,6 +33,9 @@ COMBINE = [lambda: pins.test_combine_hand_worked(GOLDEN), pins.test_combine_exac
            pins.test_combine_rounding_sensitive_cases]
 DISPATCH = [pins.test_bf16_dispatch_rows_are_bitwise_copies,
             pins.test_fp8_dispatch_rows_are_quantised_tokens]
+DEDUP = [lambda: pins.test_dedup_hand_worked(GOLDEN),
+         lambda: pins.test_dedup_random_against_cumsum_and_invariants(1),
+         lambda: pins.test_dedup_random_against_cumsum_and_invariants(4)]
 LL = [lambda: pins.test_ll_layout_hand_worked(GOLDEN),
       lambda: pins.test_ll_layout_random_against_library_routines(1),
       lambda: pins.test_ll_layout_random_against_library_routines(4),
@@ -102,6 +105,16 @@ MUTANTS = [
      "{ uint32_t u_; memcpy(&u_, &acc, 4); out[t * H + h] = (uint16_t)(u_ >> 16); }", COMBINE),
     ("combine weight of the wrong slot", "acc = fmaf(w[t * K + k],",
      "acc = fmaf(w[t * K + (K - 1 - k)],", COMBINE),
+    ("dedup offsets inclusive", "ptok_off[p + 1] = ptok_off[p] + cnt_p[p];",
+     "ptok_off[p + 1] = ptok_off[p] + cnt_p[p] + (p == 0);", DEDUP),
+    ("dedup partition by modulo", "if (v >= 0 && v < E && v / Ep == p)\n                    member = 1;",
+     "if (v >= 0 && v < E && v % P == p)\n                    member = 1;", DEDUP),
+    ("dedup global expert ids", "dd_idx[(int64_t)r * K + k] = (int32_t)(v - (int64_t)p * Ep);",
+     "dd_idx[(int64_t)r * K + k] = (int32_t)v;", DEDUP),
+    ("dedup slot map from the slot's token row in partition 0",
+     "slot_src[r] = dd_row[(int64_t)t * P + v / Ep];", "slot_src[r] = dd_row[(int64_t)t * P + 0];", DEDUP),
+    ("dedup unused rows keep a token", "    for (int64_t r = 0; r < RD; ++r) {\n        dd_src[r] = -1;",
+     "    for (int64_t r = 0; r < RD; ++r) {\n        dd_src[r] = 0;", DEDUP),
     ("ll capacity off by one", "if (rank < C) {", "if (rank <= C) {", LL),
     ("ll rows strided by top-k", "row = (int32_t)v * C + rank;",
      "row = (int32_t)v * K + rank;", LL),
@@ -117,7 +130,7 @@ MUTANTS = [
 
 
 GROUPS = {"E4M3": E4M3, "BF16": BF16, "LAYOUT": LAYOUT, "QUANT": QUANT,
-          "COMBINE": COMBINE, "DISPATCH": DISPATCH, "LL": LL}
+          "COMBINE": COMBINE, "DISPATCH": DISPATCH, "LL": LL, "DEDUP": DEDUP}
 
 
 def _group_name(checks):

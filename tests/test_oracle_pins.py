@@ -327,6 +327,105 @@ def test_ll_dispatch_rows_are_copies_and_holes_untouched():
 
 
 # ---------------------------------------------------------------------------
+# de-duplicated per-partition dispatch
+# ---------------------------------------------------------------------------
+
+DEDUP_KEYS = ["partition_token_offsets", "dedup_row", "dedup_src_token", "dedup_topk_idx",
+              "slot_src_row", "num_dedup_rows"]
+
+
+def test_dedup_hand_worked(golden_dir):
+    g = _read_kv(os.path.join(golden_dir, "dedup_hand_worked.txt"))
+    T, K, E, P = (int(g[k][0]) for k in "TKEP")
+    idx = np.array(g["topk_idx"], np.int64).reshape(T, K)
+    got = oracle.dedup_layout(idx, E, P)
+    for key in ["partition_token_offsets", "dedup_row", "dedup_src_token", "dedup_topk_idx",
+                "slot_src_row"]:
+        np.testing.assert_array_equal(np.asarray(got[key]).reshape(-1),
+                                      np.array(g[key], np.int32), err_msg=key)
+    assert got["num_dedup_rows"] == 4
+
+
+@pytest.mark.parametrize("T,K", [(1, 4), (2, 2), (3, 1), (1, 2), (5, 1)])
+def test_dedup_exhaustive_small(T, K):
+    """Every routing tensor of this shape with ids in {-1, 0, 1, 2, 3} (E = 4),
+    P in {1, 2, 4}, against the cumsum formulation."""
+    E = 4
+    n = T * K
+    grid = np.array(np.meshgrid(*[np.arange(-1, E)] * n, indexing="ij")).reshape(n, -1).T
+    batch = grid.reshape(-1, T, K).astype(np.int64)
+    for P in (1, 2, 4):
+        for i in range(batch.shape[0]):
+            got = oracle.dedup_layout(batch[i], E, P)
+            want = bf.dedup_layout(batch[i], E, P)
+            for key in DEDUP_KEYS:
+                assert np.array_equal(np.asarray(got[key]), np.asarray(want[key])), (key, batch[i], P)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_dedup_random_against_cumsum_and_invariants(seed):
+    rng = np.random.default_rng(2000 + seed)
+    E = int(rng.choice([4, 8, 16, 64, 256]))
+    P = int(rng.choice([d for d in (1, 2, 4, 8, 32, 64) if E % d == 0]))
+    K = int(rng.integers(1, min(E, 8) + 1))
+    T = int(rng.integers(1, 300))
+    c = wl.random_case(T, 8, E, P, K, 3000 + seed, masked_frac=0.1 * (seed % 3),
+                       invalid_frac=0.05 * (seed % 2), allow_dup=bool(seed % 2),
+                       skew=float(seed % 4), with_y=False)
+    got = oracle.dedup_layout(c.topk_idx, E, P)
+    want = bf.dedup_layout(c.topk_idx, E, P)
+    for key in DEDUP_KEYS:
+        np.testing.assert_array_equal(np.asarray(got[key]), np.asarray(want[key]), err_msg=key)
+    # invariants: one row per (token, member partition); rows of p contiguous and token-ordered;
+    # every valid slot's row holds its local expert id; slot_src agrees with recv_src_token
+    Ep = E // P
+    in_part = got["is_token_in_partition"]
+    rows = got["dedup_row"]
+    RD = got["num_dedup_rows"]
+    assert RD == int(in_part.sum())
+    assert sorted(rows[rows >= 0].tolist()) == list(range(RD))
+    for p in range(P):
+        seg = got["dedup_src_token"][got["partition_token_offsets"][p]:got["partition_token_offsets"][p + 1]]
+        assert np.all(np.diff(seg) > 0)
+    assert np.all(got["dedup_src_token"][RD:] == -1)
+    dst = got["dst_row"]
+    N = got["expert_offsets"][E]
+    for t in range(T):
+        for k in range(K):
+            r = dst[t, k]
+            if r < 0:
+                continue
+            e = int(c.topk_idx[t, k])
+            d = got["slot_src_row"][r]
+            assert d == rows[t, e // Ep] >= 0
+            assert got["dedup_topk_idx"][d, k] == e - (e // Ep) * Ep
+            assert got["dedup_src_token"][d] == got["recv_src_token"][r] == t
+    assert np.all(got["slot_src_row"][N:] == -1)
+
+
+def test_dedup_saves_copies_under_group_limited_gating():
+    """At the prefill shape, group-limited routing sends fewer copies per token
+    than slots (the point of de-duplication)."""
+    cfg = wl.CONFIGS["prefill"]
+    idx, _, _ = wl.route(cfg, T=512)
+    got = oracle.dedup_layout(idx, cfg["E"], cfg["P"])
+    per_token = got["num_dedup_rows"] / 512
+    assert 6.0 < per_token < 8.0, per_token
+
+
+def test_dedup_dispatch_rows_are_token_copies():
+    c = wl.random_case(80, 384, 16, 4, 4, 41, masked_frac=0.1, allow_dup=True, fp8=True)
+    res = oracle.run_dedup(c.topk_idx, c.x_bits, 16, 4, fp8=True)
+    q, s = oracle.quantize(c.x_bits)
+    src = res["dedup_src_token"]
+    live = src >= 0
+    np.testing.assert_array_equal(res["dedup_x"][live], q[src[live]])
+    np.testing.assert_array_equal(res["dedup_scales"][live], s[src[live]])
+    resb = oracle.run_dedup(c.topk_idx, c.x_bits, 16, 4, fp8=False)
+    np.testing.assert_array_equal(resb["dedup_x"][live], c.x_bits[src[live]])
+
+
+# ---------------------------------------------------------------------------
 # FP8 quantiser
 # ---------------------------------------------------------------------------
 
