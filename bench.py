@@ -51,6 +51,7 @@ KERNEL_SOURCES = {
     "ll_dispatch": ["ep_dispatch.hip", "ep_device.h", "ep_internal.h"],
     "layout_dispatch": ["ep_dispatch.hip", "ep_device.h", "ep_internal.h"],
     "layout_count": ["ep_layout.hip", "ep_device.h", "ep_internal.h"],
+    "dispatch_dedup": ["ep_dispatch.hip", "ep_device.h", "ep_internal.h"],
 }
 
 
@@ -80,6 +81,20 @@ def ll_algorithmic_bytes(T, H, E, K, C, fp8, filled):
         + (filled * G * 4 if fp8 else 0) + E * C * 4 + T * K * 4 + E * 4 + 8
     combine = filled * H * 2 + T * K * 4 + T * K * 4 + T * H * 2
     return dict(ll_dispatch=dispatch, combine=combine, total=dispatch + combine)
+
+
+def dedup_algorithmic_bytes(T, H, E, P, K, fp8, nd):
+    """The de-duplicated path's bytes: the routing read once, the layout
+    outputs, x read once, the nd used rows (codes or bf16, scales, source
+    token, K local ids) written once, and the slot-row map and dst_row."""
+    G = H // 128
+    layout = T * K * 8 + T * P + 4 * (E + P + (E + 1) + 2 * (P + 1))
+    dispatch = T * H * 2 + nd * H * (1 if fp8 else 2) + (nd * G * 4 if fp8 else 0) + nd * 4 \
+        + nd * K * 4 + T * K * 4 * 2
+    R = T * K
+    combine = R * H * 2 + R * 4 + R * 4 + T * H * 2
+    return dict(dispatch_dedup=layout + dispatch, combine=combine,
+                total=layout + dispatch + combine)
 
 
 def kernel_source_hash(kernel):
@@ -161,6 +176,8 @@ def main():
                     help="steps captured back to back in the one graph (--graph)")
     ap.add_argument("--two-calls", action="store_true",
                     help="layout and dispatch as two calls instead of ep_layout_dispatch")
+    ap.add_argument("--dedup", action="store_true",
+                    help="time ep_dispatch_dedup (one copy per token and partition) + combine")
     ap.add_argument("--low-latency", action="store_true",
                     help="time the single-launch fixed-capacity decode path")
     ap.add_argument("--capacity", type=int, default=0,
@@ -226,7 +243,18 @@ def main():
             torch.empty((R, H // 128), dtype=torch.float32, device=dev) if fp8 else None,
             torch.empty(R, dtype=torch.int32, device=dev),
             torch.empty((T, K), dtype=torch.int32, device=dev))
-        if args.two_calls:
+        if args.dedup:
+            Kp = min(K, P)
+            ddo = ep.DedupDispatched(
+                torch.empty(P + 1, dtype=torch.int32, device=dev),
+                torch.empty((T * Kp, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev),
+                torch.empty((T * Kp, H // 128), dtype=torch.float32, device=dev) if fp8 else None,
+                torch.empty(T * Kp, dtype=torch.int32, device=dev),
+                torch.empty((T * Kp, K), dtype=torch.int32, device=dev),
+                torch.empty(T * K, dtype=torch.int32, device=dev), disp.dst_row)
+            calls = [("dispatch_dedup", lambda: ep.dispatch_dedup(
+                x, idx, E, P, workspace=ws, fp8=fp8, out_layout=lay, out=ddo))]
+        elif args.two_calls:
             calls = [("layout", lambda: ep.get_dispatch_layout(idx, E, P, workspace=ws, out=lay)),
                      ("dispatch", lambda: ep.dispatch(x, idx, E, P, ws, fp8=fp8, out=disp))]
         else:
@@ -316,6 +344,9 @@ def main():
     if args.low_latency:
         filled = int((lld.recv_src_token >= 0).sum().item())
         nb = ll_algorithmic_bytes(T, H, E, K, C, fp8, filled)
+    elif args.dedup:
+        nd = int(ddo.partition_token_offsets[-1].item())
+        nb = dedup_algorithmic_bytes(T, H, E, P, K, fp8, nd)
     else:
         nb = algorithmic_bytes(T, H, E, P, K, fp8)
     value = nb["total"] / (ms_per_step * 1e-3) / 1e9
@@ -392,7 +423,8 @@ def main():
                    "tokens": T, "hidden": H, "experts": E, "partitions": P, "topk": K,
                    "fp8_dispatch": fp8, "parallelism": "single GPU",
                    "path": "low_latency" if args.low_latency else
-                           ("offsets, two calls" if args.two_calls else "offsets, one call")},
+                           ("de-duplicated per partition" if args.dedup else
+                            ("offsets, two calls" if args.two_calls else "offsets, one call"))},
         "algorithmic_bytes": nb,
         "breakdown_us": dict({name: q(v) for name, v in call_us.items()},
                              step_with_events=q(tot_us)),

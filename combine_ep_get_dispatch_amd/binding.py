@@ -48,6 +48,9 @@ SIGNATURES = {
     "ep_layout_dispatch": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _i32, ctypes.c_int,
                                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                           _vp]),
+    "ep_dispatch_dedup": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _i32, ctypes.c_int,
+                                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         _vp, _vp, _sz, _vp]),
     "ep_low_latency_dispatch": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _i32,
                                                ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ep_get_device_error": (ctypes.c_int, [_vp, _sz, ctypes.POINTER(_i64), _vp]),
@@ -269,6 +272,78 @@ def layout_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int,
         _ptr(lo.is_token_in_partition), _ptr(lo.expert_offsets), _ptr(lo.partition_offsets),
         _ptr(out.recv_x), _ptr(out.recv_scales) if fp8 else None, _ptr(out.recv_src_token),
         _ptr(out.dst_row), _ptr(workspace), workspace.numel(), _stream(x)), "ep_layout_dispatch")
+    return out_layout, out
+
+
+@dataclass
+class DedupDispatched:
+    partition_token_offsets: torch.Tensor  # [P+1] int32
+    recv_x: torch.Tensor                   # [T*Kp, H] bf16, or uint8 E4M3 codes
+    recv_scales: torch.Tensor | None       # [T*Kp, H/128] float32 (FP8 only)
+    recv_src_token: torch.Tensor           # [T*Kp] int32, -1 past the rows used
+    recv_topk_idx: torch.Tensor            # [T*Kp, K] int32 local expert ids or -1
+    slot_src_row: torch.Tensor             # [T*K] int32
+    dst_row: torch.Tensor                  # [T, K] int32
+
+
+def dispatch_dedup(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int,
+                   num_partitions: int, workspace: torch.Tensor | None = None,
+                   fp8: bool = False, out_layout: Layout | None = None,
+                   out: DedupDispatched | None = None):
+    """ep_dispatch_dedup: one copy of each token per partition it reaches.
+    Returns (Layout, DedupDispatched)."""
+    if x.dim() != 2 or topk_idx.dim() != 2:
+        raise ValueError("x must be [T, H] and topk_idx [T, K]")
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    E, P = int(num_experts), int(num_partitions)
+    Kp = min(K, P)
+    RD = T * Kp
+    _need(x, torch.bfloat16, "x")
+    _need(topk_idx, torch.int64, "topk_idx", (T, K))
+    dev = x.device
+    if workspace is None:
+        workspace = new_workspace(T, K, E, P, dev)
+    _need(workspace, torch.uint8, "workspace")
+    if out_layout is None:
+        out_layout = Layout(torch.empty(E, dtype=torch.int32, device=dev),
+                            torch.empty(P, dtype=torch.int32, device=dev),
+                            torch.empty((T, P), dtype=torch.uint8, device=dev),
+                            torch.empty(E + 1, dtype=torch.int32, device=dev),
+                            torch.empty(P + 1, dtype=torch.int32, device=dev), workspace)
+    else:
+        out_layout.workspace = workspace
+    if out is None:
+        out = DedupDispatched(
+            torch.empty(P + 1, dtype=torch.int32, device=dev),
+            torch.empty((RD, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev),
+            torch.empty((RD, H // 128), dtype=torch.float32, device=dev) if fp8 else None,
+            torch.empty(RD, dtype=torch.int32, device=dev),
+            torch.empty((RD, K), dtype=torch.int32, device=dev),
+            torch.empty(T * K, dtype=torch.int32, device=dev),
+            torch.empty((T, K), dtype=torch.int32, device=dev))
+    lo = out_layout
+    _need(lo.num_tokens_per_expert, torch.int32, "num_tokens_per_expert", (E,))
+    _need(lo.num_tokens_per_partition, torch.int32, "num_tokens_per_partition", (P,))
+    _need(lo.is_token_in_partition, torch.uint8, "is_token_in_partition", (T, P))
+    _need(lo.expert_offsets, torch.int32, "expert_offsets", (E + 1,))
+    _need(lo.partition_offsets, torch.int32, "partition_offsets", (P + 1,))
+    _need(out.partition_token_offsets, torch.int32, "partition_token_offsets", (P + 1,))
+    _need(out.recv_x, torch.uint8 if fp8 else torch.bfloat16, "recv_x", (RD, H))
+    if fp8:
+        _need(out.recv_scales, torch.float32, "recv_scales", (RD, H // 128))
+    _need(out.recv_src_token, torch.int32, "recv_src_token", (RD,))
+    _need(out.recv_topk_idx, torch.int32, "recv_topk_idx", (RD, K))
+    _need(out.slot_src_row, torch.int32, "slot_src_row", (T * K,))
+    _need(out.dst_row, torch.int32, "dst_row", (T, K))
+    _check(lib().ep_dispatch_dedup(
+        _ptr(x), T, H, _ptr(topk_idx), K, E, P, EP_DTYPE_FP8_E4M3 if fp8 else EP_DTYPE_BF16,
+        _ptr(lo.num_tokens_per_expert), _ptr(lo.num_tokens_per_partition),
+        _ptr(lo.is_token_in_partition), _ptr(lo.expert_offsets), _ptr(lo.partition_offsets),
+        _ptr(out.partition_token_offsets), _ptr(out.recv_x),
+        _ptr(out.recv_scales) if fp8 else None, _ptr(out.recv_src_token),
+        _ptr(out.recv_topk_idx), _ptr(out.slot_src_row), _ptr(out.dst_row), _ptr(workspace),
+        workspace.numel(), _stream(x)), "ep_dispatch_dedup")
     return out_layout, out
 
 

@@ -110,6 +110,40 @@ ep_status_t ep_layout_dispatch(const void* x, int32_t num_tokens, int32_t hidden
         static_cast<hipStream_t>(stream)));
 }
 
+ep_status_t ep_dispatch_dedup(const void* x, int32_t num_tokens, int32_t hidden,
+                              const int64_t* topk_idx, int32_t num_topk, int32_t num_experts,
+                              int32_t num_partitions, ep_dtype_t out_dtype,
+                              int32_t* num_tokens_per_expert, int32_t* num_tokens_per_partition,
+                              uint8_t* is_token_in_partition, int32_t* expert_offsets,
+                              int32_t* partition_offsets, int32_t* partition_token_offsets,
+                              void* recv_x, float* recv_scales, int32_t* recv_src_token,
+                              int32_t* recv_topk_idx, int32_t* slot_src_row, int32_t* dst_row,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    const int32_t T = num_tokens, H = hidden, K = num_topk, E = num_experts, P = num_partitions;
+    ep_status_t st = check_routing_shape(T, K, E, P);
+    if (st != EP_OK) return st;
+    if (out_dtype != EP_DTYPE_BF16 && out_dtype != EP_DTYPE_FP8_E4M3) return EP_ERR_INVALID_ARG;
+    const bool fp8 = out_dtype == EP_DTYPE_FP8_E4M3;
+    if (H <= 0 || H % 8 != 0 || (fp8 && H % 128 != 0)) return EP_ERR_INVALID_ARG;
+    if (!num_tokens_per_expert || !num_tokens_per_partition || !expert_offsets ||
+        !partition_offsets || !partition_token_offsets || !workspace)
+        return EP_ERR_INVALID_ARG;
+    if (T > 0) {
+        if (!x || !topk_idx || !is_token_in_partition || !recv_x || !recv_src_token ||
+            !recv_topk_idx || !slot_src_row || !dst_row)
+            return EP_ERR_INVALID_ARG;
+        if (fp8 && !recv_scales) return EP_ERR_INVALID_ARG;
+        if (!aligned16(x) || !aligned16(recv_x)) return EP_ERR_INVALID_ARG;
+    }
+    const ep::WsMap m = ep::ws_map(T, K, E, P);
+    if (workspace_bytes < m.total) return EP_ERR_WORKSPACE;
+    return from_hip(ep::launch_dispatch_dedup(
+        static_cast<const uint16_t*>(x), topk_idx, T, H, K, E, P, fp8, workspace, m,
+        num_tokens_per_expert, num_tokens_per_partition, is_token_in_partition, expert_offsets,
+        partition_offsets, partition_token_offsets, recv_x, recv_scales, recv_src_token,
+        recv_topk_idx, slot_src_row, dst_row, static_cast<hipStream_t>(stream)));
+}
+
 ep_status_t ep_low_latency_dispatch(const void* x, int32_t num_tokens, int32_t hidden,
                                     const int64_t* topk_idx, int32_t num_topk,
                                     int32_t num_experts, int32_t capacity, ep_dtype_t out_dtype,

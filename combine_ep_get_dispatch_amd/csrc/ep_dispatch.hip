@@ -29,6 +29,11 @@
 namespace ep {
 namespace {
 
+// Partition of expert e: (e * ceil(2^32 / Ep)) >> 32, exact for E <= 1024.
+__device__ __forceinline__ int partition_of_expert(int e, uint64_t pmagic) {
+    return (int)(((uint64_t)(uint32_t)e * pmagic) >> 32);
+}
+
 // One lane's share of one 1024-channel chunk of a token, ready to store.
 // FP8: lane l holds the 16 codes of channels [16l, 16l + 16) of the chunk (its
 // 128-channel group is lanes 8g .. 8g+7; the group's scale goes to s_scale).
@@ -191,7 +196,7 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void dispatch_kernel(
     scatter_token<FP8>(x, H, K, t, drow, first, recv_x, recv_scales, s_scale, nchunk);
 }
 
-// Dispatch that also finishes the layout (after layout_count_kernel<true>).
+// Dispatch that also finishes the layout (after the count launch in kCountPre mode).
 // Slot (t,k) of expert e, in token block b, with rank r inside the block:
 //   row = expert_offsets[e] + (rows of e in blocks < b) + r
 //       = sum over blocks j of pre[j][e] + sum over j < b of cnt[j][e] + r,
@@ -281,6 +286,167 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void layout_dispatch_kernel(
     ChunkData first;
     if (wave < nchunk) first = load_chunk<FP8>(x, H, t, wave, s_scale);
     scatter_token<FP8>(x, H, K, t, drow, first, recv_x, recv_scales, s_scale, nchunk);
+}
+
+// De-duplicated per-partition dispatch (after the count launch in kCountDedup
+// mode): one copy of the token per partition it reaches, at partition p's
+// row  sum over blocks j of ppre[j][p] + sum over j < b of pcnt[j][p] + (the
+// token's rank among its block's member tokens of p), and the expert-major
+// row of every slot as in layout_dispatch_kernel (only as an index: the
+// data goes to the de-duplicated rows).  Thread i = g * S + j sums block j's
+// terms (and every S-th block's after it) for slot g (g < K: its expert row
+// and its partition row) or for the totals (g = K: N and the number of
+// de-duplicated rows); shuffle reductions over S-lane segments close the
+// sums.  A slot stores the token's data only if it is the first of
+// the token's slots in its partition.  Workgroup 0 writes the counts, offsets
+// and header.
+template <bool FP8>
+__global__ __launch_bounds__(kDispatchMaxThreads) void dedup_dispatch_kernel(
+    const uint16_t* __restrict__ x, int H, int K, int E, int P, int Ep, uint64_t pmagic, int TB,
+    int nb, int seg_log2, int Kp, const int* __restrict__ cnt, const int* __restrict__ pre,
+    const int* __restrict__ pcnt, const int* __restrict__ ppre, const int* __restrict__ inv,
+    const int* __restrict__ rows, const int* __restrict__ prank, WsHeader* __restrict__ hdr,
+    int32_t* __restrict__ cnt_e, int32_t* __restrict__ cnt_p, int32_t* __restrict__ off_e,
+    int32_t* __restrict__ off_p, int32_t* __restrict__ ptok_off, void* __restrict__ recv_x,
+    float* __restrict__ recv_scales, int32_t* __restrict__ recv_src,
+    int32_t* __restrict__ recv_topk_idx, int32_t* __restrict__ slot_src,
+    int32_t* __restrict__ dst_row, int nchunk, int nrows, int ndrows) {
+    extern __shared__ float s_scale[];   // [G] scales of this token (FP8)
+    __shared__ int s_pk[64];             // packed slot k (K <= 64)
+    __shared__ int s_erow[64];           // expert-major row of slot k
+    __shared__ int s_drow[64];           // de-duplicated row of slot k's partition
+    __shared__ int s_n, s_nd;            // N and the number of de-duplicated rows
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int t = blockIdx.x;
+
+    {
+        const int b = t / TB;
+        const int S = 1 << seg_log2;
+        const int g = tid >> seg_log2;       // slot g (g < K), or the totals (g == K)
+        const int j0 = tid & (S - 1);
+        int ve = 0, vp = 0, pk = -1, pr = -1;
+        if (g < K) {
+            pk = rows[(int64_t)t * K + g];
+            if (pk >= 0) {
+                const int e = pk >> kRankBits;
+                const int p = partition_of_expert(e, pmagic);
+                pr = prank[(int64_t)t * K + g];
+                for (int j = j0; j < nb; j += S) {
+                    ve += pre[(int64_t)j * (E + 1) + e];
+                    vp += ppre[(int64_t)j * (P + 1) + p];
+                    if (j < b) {
+                        ve += cnt[(int64_t)j * E + e];
+                        vp += pcnt[(int64_t)j * P + p];
+                    }
+                }
+            }
+        } else if (g == K) {
+            for (int j = j0; j < nb; j += S) {
+                ve += pre[(int64_t)j * (E + 1) + E];
+                vp += ppre[(int64_t)j * (P + 1) + P];
+            }
+        }
+        for (int o = S >> 1; o >= 1; o >>= 1) {
+            ve += __shfl_xor(ve, o);
+            vp += __shfl_xor(vp, o);
+        }
+        if (j0 == 0) {
+            if (g < K) {
+                int r = pk >= 0 ? ve + (pk & ((1 << kRankBits) - 1)) : -1;
+                if (r >= nrows) r = -1;    // only with a workspace from another layout
+                s_erow[g] = r;
+                s_pk[g] = pk;
+                int d = (pk >= 0 && pr >= 0) ? vp + pr : -1;
+                if (d >= ndrows) d = -1;
+                s_drow[g] = d;
+            } else if (g == K) {
+                s_n = ve;
+                s_nd = vp;
+            }
+        }
+    }
+    __syncthreads();
+    const int N = s_n;
+    const int ND = s_nd;
+    const int pk = lane < K ? s_pk[lane] : -1;
+    const int e = pk >= 0 ? pk >> kRankBits : -1;
+    const int part = e >= 0 ? partition_of_expert(e, pmagic) : -1;
+    const int erow = lane < K ? s_erow[lane] : -1;
+    const int drow = lane < K ? s_drow[lane] : -1;
+    bool first = part >= 0;
+    for (int j = 0; j < K; ++j) {
+        const int pj = __builtin_amdgcn_readlane(part, j);
+        if (j < lane && pj == part) first = false;
+    }
+    const int store_row = first ? drow : -1;
+
+    if (wave == 0) {
+        if (lane < K) {
+            dst_row[(int64_t)t * K + lane] = erow;
+            if (erow >= 0) slot_src[erow] = drow;
+            const int r = t * K + lane;    // expert rows past N belong to no slot
+            if (r >= N) slot_src[r] = -1;
+            if (store_row >= 0) recv_src[store_row] = t;
+        }
+        // Local expert ids of each of this token's rows: owner slot k's row,
+        // lane j's slot.  (Spreading this and the marking below over all
+        // waves measured slower.)
+        for (int k = 0; k < K; ++k) {
+            const int rk = __builtin_amdgcn_readlane(store_row, k);
+            if (rk < 0) continue;
+            const int pk_part = __builtin_amdgcn_readlane(part, k);
+            if (lane < K)
+                recv_topk_idx[(int64_t)rk * K + lane] = (part == pk_part) ? e - pk_part * Ep : -1;
+        }
+    }
+    // Rows past the last de-duplicated one among [t*Kp, (t+1)*Kp) are unused.
+    for (int i = tid; i < Kp * (K + 1); i += blockDim.x) {
+        const int q = i / (K + 1);
+        const int c = i - q * (K + 1);
+        const int64_t r = (int64_t)t * Kp + q;
+        if (r < ND) continue;
+        if (c == K) recv_src[r] = -1;
+        else recv_topk_idx[r * K + c] = -1;
+    }
+
+    if (t == 0) {                          // the layout's own outputs
+        for (int ee = tid; ee <= E; ee += blockDim.x) {
+            int c = 0, o = 0;
+            for (int j = 0; j < nb; ++j) {
+                o += pre[(int64_t)j * (E + 1) + ee];
+                if (ee < E) c += cnt[(int64_t)j * E + ee];
+            }
+            off_e[ee] = o;
+            if (ee < E) cnt_e[ee] = c;
+            if (ee % Ep == 0) off_p[ee / Ep] = o;
+        }
+        for (int p = tid; p <= P; p += blockDim.x) {
+            int c = 0, o = 0;
+            for (int j = 0; j < nb; ++j) {
+                o += ppre[(int64_t)j * (P + 1) + p];
+                if (p < P) c += pcnt[(int64_t)j * P + p];
+            }
+            ptok_off[p] = o;
+            if (p < P) cnt_p[p] = c;
+        }
+        if (tid == 0) {
+            int64_t nerr = 0;
+            for (int j = 0; j < nb; ++j) nerr += inv[j];
+            hdr->num_valid = N;
+            hdr->num_invalid = nerr;
+        }
+    }
+
+    ChunkData first_chunk;
+    if (wave < nchunk) first_chunk = load_chunk<FP8>(x, H, t, wave, s_scale);
+    scatter_token<FP8>(x, H, K, t, store_row, first_chunk, recv_x, recv_scales, s_scale, nchunk);
+}
+
+// T = 0 for the de-duplicated dispatch: every partition token offset is 0.
+__global__ void dedup_empty_kernel(int P, int32_t* __restrict__ ptok_off) {
+    for (int i = threadIdx.x; i <= P; i += blockDim.x) ptok_off[i] = 0;
 }
 
 // Decode dispatch into fixed-capacity receive rows, in one launch (expert e
@@ -478,7 +644,7 @@ hipError_t launch_layout_dispatch(const uint16_t* x, const int64_t* idx, int T, 
         if (e != hipSuccess) return e;
         return launch_dispatch(x, T, H, K, fp8, recv_x, recv_scales, recv_src, dst_row, ws, m, s);
     }
-    hipError_t e = launch_layout_count(idx, T, K, E, P, ws, m, in_part, true, s);
+    hipError_t e = launch_layout_count(idx, T, K, E, P, ws, m, in_part, kCountPre, s);
     if (e != hipSuccess) return e;
     char* base = static_cast<char*>(ws);
     WsHeader* hdr = reinterpret_cast<WsHeader*>(base);
@@ -498,6 +664,60 @@ hipError_t launch_layout_dispatch(const uint16_t* x, const int64_t* idx, int T, 
                            E, P, E / P, m.tb, m.nb, seg_log2, cnt, pre, pcnt, inv, rows, hdr,
                            cnt_e, cnt_p, off_e, off_p, recv_x, recv_scales, recv_src, dst_row,
                            nchunk, T * K);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_dedup(const uint16_t* x, const int64_t* idx, int T, int H, int K,
+                                 int E, int P, bool fp8, void* ws, const WsMap& m, int32_t* cnt_e,
+                                 int32_t* cnt_p, uint8_t* in_part, int32_t* off_e, int32_t* off_p,
+                                 int32_t* ptok_off, void* recv_x, float* recv_scales,
+                                 int32_t* recv_src, int32_t* recv_topk_idx, int32_t* slot_src,
+                                 int32_t* dst_row, hipStream_t s) {
+    if (T == 0) {
+        hipError_t e = launch_layout(idx, T, K, E, P, ws, m, cnt_e, cnt_p, in_part, off_e, off_p,
+                                     s);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(dedup_empty_kernel, dim3(1), dim3(256), 0, s, P, ptok_off);
+        return hipGetLastError();
+    }
+    hipError_t e = launch_layout_count(idx, T, K, E, P, ws, m, in_part, kCountDedup, s);
+    if (e != hipSuccess) return e;
+    char* base = static_cast<char*>(ws);
+    WsHeader* hdr = reinterpret_cast<WsHeader*>(base);
+    const int* cnt = reinterpret_cast<const int*>(base + m.cnt_off);
+    const int* pcnt = reinterpret_cast<const int*>(base + m.pcnt_off);
+    const int* inv = reinterpret_cast<const int*>(base + m.inv_off);
+    const int* pre = reinterpret_cast<const int*>(base + m.pre_off);
+    const int* ppre = reinterpret_cast<const int*>(base + m.ppre_off);
+    const int* prank = reinterpret_cast<const int*>(base + m.prank_off);
+    const int* rows = reinterpret_cast<const int*>(base + m.rows_off);
+    const int nchunk = (H + kDispatchChunk - 1) / kDispatchChunk;
+    const int nw = nchunk < kDispatchMaxThreads / 64 ? nchunk : kDispatchMaxThreads / 64;
+    // Enough threads for at least one lane per term group, and segments of S
+    // lanes (a power of two, <= 64, no wider than the blocks need).
+    const int groups = K + 1;
+    int threads = 64 * nw;
+    if (threads < groups) threads = (groups + 63) / 64 * 64;
+    int seg_log2 = 0;
+    while ((1 << (seg_log2 + 1)) <= 64 && (groups << (seg_log2 + 1)) <= threads &&
+           (1 << seg_log2) < m.nb)
+        ++seg_log2;
+    const int Kp = K < P ? K : P;
+    const size_t lds = fp8 ? sizeof(float) * (size_t)(H / 128) : 0;
+    const uint64_t pmagic = ((uint64_t)1 << 32) / (uint64_t)(E / P) +
+                            ((((uint64_t)1 << 32) % (uint64_t)(E / P)) ? 1 : 0);
+    if (fp8)
+        hipLaunchKernelGGL(dedup_dispatch_kernel<true>, dim3(T), dim3(threads), lds, s, x, H, K,
+                           E, P, E / P, pmagic, m.tb, m.nb, seg_log2, Kp, cnt, pre, pcnt, ppre,
+                           inv, rows, prank, hdr, cnt_e, cnt_p, off_e, off_p, ptok_off, recv_x,
+                           recv_scales, recv_src, recv_topk_idx, slot_src, dst_row, nchunk,
+                           T * K, T * Kp);
+    else
+        hipLaunchKernelGGL(dedup_dispatch_kernel<false>, dim3(T), dim3(threads), lds, s, x, H, K,
+                           E, P, E / P, pmagic, m.tb, m.nb, seg_log2, Kp, cnt, pre, pcnt, ppre,
+                           inv, rows, prank, hdr, cnt_e, cnt_p, off_e, off_p, ptok_off, recv_x,
+                           recv_scales, recv_src, recv_topk_idx, slot_src, dst_row, nchunk,
+                           T * K, T * Kp);
     return hipGetLastError();
 }
 

@@ -46,14 +46,19 @@ static_assert(sizeof(WsHeader) <= kWsHeaderBytes, "header too large");
 //   inv  int32 [nb]    per-block invalid-slot counts
 //   pre  int32 [nb][E+1] per-block exclusive prefix of the expert counts over
 //                      the experts, pre[b][E] = the block's valid slots
-//                      (written only by the single-call layout + dispatch)
+//                      (written only by the one-call and de-duplicated paths)
+//   ppre int32 [nb][P+1] per-block exclusive prefix of the partition token
+//                      counts over the partitions (de-duplicated path)
+//   prank int32 [T*K]  each slot's rank among its block's member tokens of
+//                      the slot's partition (de-duplicated path)
 //   rows int32 [T*K]   receive row of every slot (-1 if masked/invalid); the
 //                      count kernel leaves (expert << 12 | rank in block)
 //                      there and the finalize kernel turns it into the row
 struct WsMap {
     int nb = 0;        // token blocks
     int tb = 1;        // tokens per block
-    size_t cnt_off = 0, pcnt_off = 0, inv_off = 0, pre_off = 0, rows_off = 0, total = 0;
+    size_t cnt_off = 0, pcnt_off = 0, inv_off = 0, pre_off = 0, ppre_off = 0, prank_off = 0;
+    size_t rows_off = 0, total = 0;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -66,7 +71,9 @@ inline WsMap ws_map(int T, int K, int E, int P) {
     m.pcnt_off = m.cnt_off + align256(sizeof(int32_t) * (size_t)E * (size_t)m.nb);
     m.inv_off = m.pcnt_off + align256(sizeof(int32_t) * (size_t)P * (size_t)m.nb);
     m.pre_off = m.inv_off + align256(sizeof(int32_t) * (size_t)m.nb);
-    m.rows_off = m.pre_off + align256(sizeof(int32_t) * (size_t)(E + 1) * (size_t)m.nb);
+    m.ppre_off = m.pre_off + align256(sizeof(int32_t) * (size_t)(E + 1) * (size_t)m.nb);
+    m.prank_off = m.ppre_off + align256(sizeof(int32_t) * (size_t)(P + 1) * (size_t)m.nb);
+    m.rows_off = m.prank_off + align256(sizeof(int32_t) * (size_t)T * (size_t)K);
     m.total = m.rows_off + align256(sizeof(int32_t) * (size_t)T * (size_t)K);
     return m;
 }
@@ -82,11 +89,18 @@ hipError_t launch_layout(const int64_t* idx, int T, int K, int E, int P, void* w
 // True when launch_layout takes its single-launch form for this shape.
 bool layout_single_launch(int T, int K, int E, int P, const WsMap& m);
 
-// The first of the two layout launches alone (T > 0): per-block counts,
-// partition rows and counts, invalid counts, packed (expert << 12 | rank)
-// slots, and with `with_pre` the per-block prefix matrix.
+// What the count launch writes besides the per-block counts, partition rows
+// and counts, invalid counts and packed (expert << 12 | rank) slots:
+// kCountPlain nothing more; kCountPre each block's prefix of its expert
+// counts; kCountDedup also every slot's in-block rank among its partition's
+// member tokens and each block's prefix of its partition counts.
+constexpr int kCountPlain = 0;
+constexpr int kCountPre = 1;
+constexpr int kCountDedup = 2;
+
+// The first of the two layout launches alone (T > 0), in one of the modes above.
 hipError_t launch_layout_count(const int64_t* idx, int T, int K, int E, int P, void* ws,
-                               const WsMap& m, uint8_t* in_part, bool with_pre, hipStream_t s);
+                               const WsMap& m, uint8_t* in_part, int mode, hipStream_t s);
 
 // ---------------------------------------------------------------- dispatch --
 // One workgroup per token, one wave per 1024-channel chunk (16 channels per
@@ -131,6 +145,17 @@ hipError_t launch_ll_dispatch(const uint16_t* x, const int64_t* idx, int T, int 
                               int C, bool fp8, int32_t* cnt_e, void* recv_x, float* recv_scales,
                               int32_t* recv_src, int32_t* dst_row, int64_t* num_invalid,
                               hipStream_t s);
+
+// De-duplicated per-partition dispatch: the count launch in kCountDedup mode,
+// then one dispatch launch that finishes both layouts (expert-major slot rows
+// and de-duplicated partition rows) and writes one copy of each token per
+// partition it reaches.
+hipError_t launch_dispatch_dedup(const uint16_t* x, const int64_t* idx, int T, int H, int K,
+                                 int E, int P, bool fp8, void* ws, const WsMap& m, int32_t* cnt_e,
+                                 int32_t* cnt_p, uint8_t* in_part, int32_t* off_e, int32_t* off_p,
+                                 int32_t* ptok_off, void* recv_x, float* recv_scales,
+                                 int32_t* recv_src, int32_t* recv_topk_idx, int32_t* slot_src,
+                                 int32_t* dst_row, hipStream_t s);
 
 // ---------------------------------------------------------------- combine ---
 // One wave per (token, 512-channel chunk); 8 channels per lane; two waves per

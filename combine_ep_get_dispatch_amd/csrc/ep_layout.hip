@@ -220,11 +220,20 @@ __host__ __device__ inline int scan_per(int E) {
 // Match tables are used up to this many experts ([waves][E][2] 32-bit words).
 constexpr int kMatchTableMaxE = 256;
 
+// Ints of layout_count_kernel's partition-count array pc: P, padded with
+// zeros to 64 * scan_per(P) when it is scanned (kCountDedup).
+__host__ __device__ inline int count_pc_ints(int P, int mode) {
+    return mode == kCountDedup ? 64 * scan_per(P) : P;
+}
+
 // layout_count_kernel's dynamic LDS, in ints: wcnt [waves][E], ids and rnk
-// [kLayoutEntries] each, pc [P], with PRE bc [64 * scan_per(E)]; the match
-// tables follow at the returned offset.
-__host__ __device__ inline int count_table_offset(int E, int P, bool pre) {
-    return kLayoutWaves * E + 2 * kLayoutEntries + P + (pre ? 64 * scan_per(E) : 0);
+// [kLayoutEntries] each, pc [count_pc_ints], with kCountPre or kCountDedup bc
+// [64 * scan_per(E)], with kCountDedup the partition ballots wb [waves][128];
+// the match tables follow at the returned offset.
+__host__ __device__ inline int count_table_offset(int E, int P, int mode) {
+    return kLayoutWaves * E + 2 * kLayoutEntries + count_pc_ints(P, mode) +
+           (mode != kCountPlain ? 64 * scan_per(E) : 0) +
+           (mode == kCountDedup ? kLayoutWaves * 128 : 0);
 }
 
 // Partition of expert e: e / Ep computed as (e * ceil(2^32 / Ep)) >> 32,
@@ -274,6 +283,98 @@ __device__ void partition_rows(const Id* ids, int ntok, int K, int P, uint64_t p
                 }
             }
         }
+    }
+}
+
+// Partition-membership rows of tokens [0, ntok) as partition_rows writes
+// them, plus each slot's rank among the block's member tokens of its slot's
+// partition (token order), for the de-duplicated dispatch.  Tokens go in
+// passes of one per thread; within a pass a wave's lanes are consecutive
+// tokens, so for every partition q of a 64-partition window one ballot of
+// "member of q" gives the members' ranks inside the wave.  Lane q keeps
+// partition q's ballot and stores it in the wave's LDS row wb; each slot then
+// reads the ballot of its own partition once and takes the popcount of the
+// lanes below.  An exclusive prefix over the waves (plus the earlier passes,
+// kept in pc) makes the ranks ranks inside the block.  wp is [waves][P] LDS
+// scratch, wb [waves][64][2] LDS scratch, srank [ntok*K] LDS scratch, pc [P]
+// zeroed LDS that ends holding the block's member-token count per partition;
+// prank [ntok*K] (global) receives the ranks (-1 for slots without an
+// expert).
+template <typename Id>
+__device__ void partition_ranks(const Id* ids, int ntok, int K, int P, uint64_t pmagic,
+                                uint8_t* out_rows, bool vec, int* wp, unsigned* wb, int* srank,
+                                int* pc, int* prank) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int base = 0; base < ntok; base += kLayoutThreads) {
+        for (int i = threadIdx.x; i < kLayoutWaves * P; i += kLayoutThreads) wp[i] = 0;
+        __syncthreads();
+        const int tl = base + threadIdx.x;
+        const bool act = tl < ntok;
+        for (int w0 = 0; w0 < P; w0 += 64) {
+            uint64_t mask = 0;
+            if (act) {
+                for (int k = 0; k < K; ++k) {
+                    const int e = ids[tl * K + k];
+                    if (e < 0) continue;
+                    const int q = partition_of(e, pmagic) - w0;
+                    if (q >= 0 && q < 64) mask |= 1ull << q;
+                }
+                const int nbytes = min(64, P - w0);
+                uint8_t* row = out_rows + (int64_t)tl * P + w0;
+                if (vec) {
+                    for (int q = 0; q < nbytes; q += 16) {
+                        const uint32_t b16 = (uint32_t)(mask >> q) & 0xffffu;
+                        *reinterpret_cast<uint4*>(row + q) =
+                            make_uint4(spread4(b16), spread4(b16 >> 4), spread4(b16 >> 8),
+                                       spread4(b16 >> 12));
+                    }
+                } else {
+                    for (int q = 0; q < nbytes; ++q) row[q] = (uint8_t)((mask >> q) & 1u);
+                }
+            }
+            const int nq = min(64, P - w0);
+            uint64_t mine = 0;                   // lane q: ballot of partition w0 + q
+            for (int q = 0; q < nq; ++q) {       // wave-uniform loop: ballots are safe
+                const uint64_t bb = __ballot((mask >> q) & 1ull);
+                if (lane == q) mine = bb;
+            }
+            unsigned* myb = wb + wave * 128;
+            myb[2 * lane] = (unsigned)mine;
+            myb[2 * lane + 1] = (unsigned)(mine >> 32);
+            if (lane < nq) wp[wave * P + w0 + lane] = __popcll(mine);
+            // (this wave's LDS writes above complete before its reads below)
+            if (act) {
+                for (int k = 0; k < K; ++k) {
+                    const int e = ids[tl * K + k];
+                    if (e < 0) continue;
+                    const int q = partition_of(e, pmagic) - w0;
+                    if (q < 0 || q >= 64) continue;
+                    const uint64_t bq = (uint64_t)myb[2 * q] | ((uint64_t)myb[2 * q + 1] << 32);
+                    srank[tl * K + k] = __popcll(bq & below);
+                }
+            }
+        }
+        __syncthreads();
+        for (int p = threadIdx.x; p < P; p += kLayoutThreads) {   // prefix over waves
+            int run = pc[p];
+            for (int w = 0; w < kLayoutWaves; ++w) {
+                const int c = wp[w * P + p];
+                wp[w * P + p] = run;
+                run += c;
+            }
+            pc[p] = run;
+        }
+        __syncthreads();
+        if (act) {
+            for (int k = 0; k < K; ++k) {
+                const int e = ids[tl * K + k];
+                prank[tl * K + k] =
+                    e >= 0 ? wp[wave * P + partition_of(e, pmagic)] + srank[tl * K + k] : -1;
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -368,25 +469,28 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_fused_kernel(
 
 // ------------------------------------------------------------ two launches --
 
-// PRE: also write pre[b][0..E] = the block's exclusive prefix of its expert
-// counts over the experts (pre[b][E] = the block's valid slots), so that a
-// later kernel can form any expert offset as a sum over blocks instead of a
-// scan over experts (the single-call layout + dispatch uses this).
-template <bool PRE>
+// MODE >= kCountPre: also write pre[b][0..E] = the block's exclusive prefix
+// of its expert counts over the experts (pre[b][E] = the block's valid
+// slots), so that a later kernel can form any expert offset as a sum over
+// blocks instead of a scan over experts (the one-call layout + dispatch uses
+// this).  MODE == kCountDedup: also prank (in-block partition ranks of every
+// slot) and ppre[b][0..P] (prefix of the block's partition counts).
+template <int MODE>
 __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
     const int64_t* __restrict__ idx, int T, int K, int E, int P, uint64_t pmagic, int TB,
     int ebits,
     int* __restrict__ cnt, int* __restrict__ pcnt, int* __restrict__ inv,
     int* __restrict__ rows, uint8_t* __restrict__ in_part, int vec_rows,
-    int* __restrict__ pre) {
+    int* __restrict__ pre, int* __restrict__ prank, int* __restrict__ ppre) {
+    constexpr bool PRE = MODE != kCountPlain;
     extern __shared__ int smem[];
     int* wcnt = smem;                              // [waves][E]
     int* ids = wcnt + kLayoutWaves * E;            // [kLayoutEntries] stored ids
     int* rnk = ids + kLayoutEntries;               // [kLayoutEntries]
-    int* pc = rnk + kLayoutEntries;                // [P]
-    int* bc = pc + P;                              // [64 * scan_per(E)] block counts (PRE)
+    int* pc = rnk + kLayoutEntries;                // [count_pc_ints(P, MODE)]
+    int* bc = pc + count_pc_ints(P, MODE);         // [64 * scan_per(E)] block counts (PRE)
     // [waves][E][2] match tables (E <= kMatchTableMaxE)
-    unsigned* mtab = reinterpret_cast<unsigned*>(smem + count_table_offset(E, P, PRE));
+    unsigned* mtab = reinterpret_cast<unsigned*>(smem + count_table_offset(E, P, MODE));
     const bool use_mtab = E <= kMatchTableMaxE;
     __shared__ int s_err;
 
@@ -406,7 +510,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
         v[u] = (j < n) ? my[j] : -1;
     }
     for (int i = tid; i < kLayoutWaves * E; i += kLayoutThreads) wcnt[i] = 0;
-    for (int i = tid; i < P; i += kLayoutThreads) pc[i] = 0;
+    for (int i = tid; i < count_pc_ints(P, MODE); i += kLayoutThreads) pc[i] = 0;
     if (PRE)
         for (int i = E + tid; i < 64 * scan_per(E); i += kLayoutThreads) bc[i] = 0;
     if (use_mtab)
@@ -448,9 +552,27 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
         const int e = ids[j];
         rows[(int64_t)t0 * K + j] = (e >= 0) ? (e << kRankBits) | rnk[j] : -1;
     }
-    partition_rows(ids, tb, K, P, pmagic, in_part + (int64_t)t0 * P, vec_rows != 0, pc);
-    __syncthreads();
-    for (int p = tid; p < P; p += kLayoutThreads) pcnt[(int64_t)b * P + p] = pc[p];
+    if constexpr (MODE == kCountDedup) {
+        __syncthreads();                           // rnk and wcnt are free from here
+        partition_ranks(ids, tb, K, P, pmagic, in_part + (int64_t)t0 * P, vec_rows != 0, wcnt,
+                        reinterpret_cast<unsigned*>(bc + 64 * scan_per(E)), rnk, pc,
+                        prank + (int64_t)t0 * K);    // ends with a barrier
+        if (tid < 64) {
+            int* cb = pcnt + (int64_t)b * P;
+            int* pb = ppre + (int64_t)b * (P + 1);
+            switch (scan_per(P)) {
+                case 1: scan_block_counts<1>(pc, P, cb, pb); break;
+                case 2: scan_block_counts<2>(pc, P, cb, pb); break;
+                case 4: scan_block_counts<4>(pc, P, cb, pb); break;
+                case 8: scan_block_counts<8>(pc, P, cb, pb); break;
+                default: scan_block_counts<16>(pc, P, cb, pb); break;
+            }
+        }
+    } else {
+        partition_rows(ids, tb, K, P, pmagic, in_part + (int64_t)t0 * P, vec_rows != 0, pc);
+        __syncthreads();
+        for (int p = tid; p < P; p += kLayoutThreads) pcnt[(int64_t)b * P + p] = pc[p];
+    }
     if (tid == 0) inv[b] = s_err;
 }
 
@@ -561,32 +683,51 @@ bool vector_rows(int P, const uint8_t* in_part) {
 }  // namespace
 
 // Dynamic LDS of layout_count_kernel.
-size_t count_lds_bytes(int E, int P, bool with_pre) {
-    size_t bytes = sizeof(int) * (size_t)count_table_offset(E, P, with_pre);
+size_t count_lds_bytes(int E, int P, int mode) {
+    size_t bytes = sizeof(int) * (size_t)count_table_offset(E, P, mode);
     if (E <= kMatchTableMaxE) bytes += sizeof(unsigned) * 2 * (size_t)kLayoutWaves * E;
     return bytes;
 }
 
 hipError_t launch_layout_count(const int64_t* idx, int T, int K, int E, int P, void* ws,
-                               const WsMap& m, uint8_t* in_part, bool with_pre, hipStream_t s) {
+                               const WsMap& m, uint8_t* in_part, int mode, hipStream_t s) {
     char* base = static_cast<char*>(ws);
     int* cnt = reinterpret_cast<int*>(base + m.cnt_off);
     int* pcnt = reinterpret_cast<int*>(base + m.pcnt_off);
     int* inv = reinterpret_cast<int*>(base + m.inv_off);
     int* pre = reinterpret_cast<int*>(base + m.pre_off);
+    int* ppre = reinterpret_cast<int*>(base + m.ppre_off);
+    int* prank = reinterpret_cast<int*>(base + m.prank_off);
     int* rows = reinterpret_cast<int*>(base + m.rows_off);
     const int ebits = expert_bits(E);
     const uint64_t pmagic = partition_magic(E / P);
     const int vec = vector_rows(P, in_part);
-    const size_t lds = count_lds_bytes(E, P, with_pre);
-    if (with_pre)
-        hipLaunchKernelGGL(layout_count_kernel<true>, dim3(m.nb), dim3(kLayoutThreads), lds, s,
-                           idx, T, K, E, P, pmagic, m.tb, ebits, cnt, pcnt, inv, rows, in_part,
-                           vec, pre);
+    const size_t lds = count_lds_bytes(E, P, mode);
+    if (lds > 64 * 1024) {
+        hipError_t e = hipErrorInvalidValue;
+        if (mode == kCountDedup)
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(layout_count_kernel<kCountDedup>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        else if (mode == kCountPre)
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(layout_count_kernel<kCountPre>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        else
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(layout_count_kernel<kCountPlain>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    if (mode == kCountDedup)
+        hipLaunchKernelGGL(layout_count_kernel<kCountDedup>, dim3(m.nb), dim3(kLayoutThreads), lds,
+                           s, idx, T, K, E, P, pmagic, m.tb, ebits, cnt, pcnt, inv, rows, in_part,
+                           vec, pre, prank, ppre);
+    else if (mode == kCountPre)
+        hipLaunchKernelGGL(layout_count_kernel<kCountPre>, dim3(m.nb), dim3(kLayoutThreads), lds,
+                           s, idx, T, K, E, P, pmagic, m.tb, ebits, cnt, pcnt, inv, rows, in_part,
+                           vec, pre, prank, ppre);
     else
-        hipLaunchKernelGGL(layout_count_kernel<false>, dim3(m.nb), dim3(kLayoutThreads), lds, s,
-                           idx, T, K, E, P, pmagic, m.tb, ebits, cnt, pcnt, inv, rows, in_part,
-                           vec, pre);
+        hipLaunchKernelGGL(layout_count_kernel<kCountPlain>, dim3(m.nb), dim3(kLayoutThreads), lds,
+                           s, idx, T, K, E, P, pmagic, m.tb, ebits, cnt, pcnt, inv, rows, in_part,
+                           vec, pre, prank, ppre);
     return hipGetLastError();
 }
 
@@ -622,7 +763,7 @@ hipError_t launch_layout(const int64_t* idx, int T, int K, int E, int P, void* w
         return hipGetLastError();
     }
 
-    hipError_t err = launch_layout_count(idx, T, K, E, P, ws, m, in_part, false, s);
+    hipError_t err = launch_layout_count(idx, T, K, E, P, ws, m, in_part, kCountPlain, s);
     if (err != hipSuccess) return err;
     int* cnt = reinterpret_cast<int*>(base + m.cnt_off);
     int* pcnt = reinterpret_cast<int*>(base + m.pcnt_off);

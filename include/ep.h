@@ -149,6 +149,48 @@ ep_status_t ep_layout_dispatch(const void *x, int32_t num_tokens, int32_t hidden
                                size_t workspace_bytes, void *stream);
 
 /*
+ * De-duplicated dispatch: one copy of a token per destination partition
+ * instead of one per selected expert -- what goes to the same destination is
+ * merged before it is sent ("DeepSeek Open Source Week: A carnival of
+ * technology inclusion, the magic of improving the efficiency of large
+ * models", section 4), and group-limited gating keeps the destinations per
+ * token few ("DeepSeek releases DeepEP, an efficient communication library
+ * for MoE models", section "DeepEP: Optimizing MoE Communication").  The
+ * layout is this library's (the pages give none).  Kp = min(K, P),
+ * RD = T * Kp rows (an upper bound on the rows used).
+ *   The five layout outputs as in ep_get_dispatch_layout, and
+ *   partition_token_offsets [P+1]: exclusive prefix of
+ *     num_tokens_per_partition; partition p's rows are
+ *     [partition_token_offsets[p], partition_token_offsets[p+1]), one per
+ *     token with a valid slot in p, in token order; ND = offsets[P] rows used.
+ *   recv_x [RD*H] (bf16, or E4M3 codes with recv_scales [RD*G] as in
+ *     ep_dispatch): row r holds token recv_src_token[r]; rows >= ND are not
+ *     written and get recv_src_token = -1.
+ *   recv_topk_idx [RD*K] int32: for row r of (t, p) and each slot k of t, the
+ *     local expert id e - p*(E/P) if slot k's expert e is in p, else -1 (all
+ *     -1 for rows >= ND): the per-row local-expert selection.
+ *   dst_row [T*K]: every valid slot's expert-major row, exactly as
+ *     ep_dispatch numbers them (only an index here: no data is written there).
+ *   slot_src_row [T*K] int32: for every expert-major row r, the
+ *     de-duplicated row holding its token (-1 for r >= N), so expert e's
+ *     inputs are the rows slot_src_row[expert_offsets[e] ..
+ *     expert_offsets[e+1]) -- the per-partition local permutation.
+ * ep_combine then runs unchanged on expert outputs y [T*K, H] in expert-major
+ * order with dst_row.  Two kernel launches; the workspace is sized by
+ * ep_workspace_bytes and afterwards serves ep_get_device_error (not a later
+ * ep_dispatch).
+ */
+ep_status_t ep_dispatch_dedup(const void *x, int32_t num_tokens, int32_t hidden,
+                              const int64_t *topk_idx, int32_t num_topk, int32_t num_experts,
+                              int32_t num_partitions, ep_dtype_t out_dtype,
+                              int32_t *num_tokens_per_expert, int32_t *num_tokens_per_partition,
+                              uint8_t *is_token_in_partition, int32_t *expert_offsets,
+                              int32_t *partition_offsets, int32_t *partition_token_offsets,
+                              void *recv_x, float *recv_scales, int32_t *recv_src_token,
+                              int32_t *recv_topk_idx, int32_t *slot_src_row, int32_t *dst_row,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Combine (the "combine" half of "DeepEP: Optimizing MoE Communication"):
  * bring each token's expert outputs back and reduce them with its gate
  * weights.  For every token t and channel h:

@@ -46,13 +46,13 @@ def test_status_strings():
 
 def test_workspace_bytes():
     L = b.lib()
-    # header + cnt [nb][E] + pcnt [nb][P] + inv [nb] + pre [nb][E+1] + rows [T*K],
-    # each rounded up to 256 bytes
+    # header + cnt [nb][E] + pcnt [nb][P] + inv [nb] + pre [nb][E+1] + ppre [nb][P+1]
+    # + prank [T*K] + rows [T*K], each rounded up to 256 bytes
     tb = 2048 // 8
     nb = -(-4096 // tb)
     r256 = lambda v: -(-v // 256) * 256
     want = 256 + r256(4 * 256 * nb) + r256(4 * 64 * nb) + r256(4 * nb) + r256(4 * 257 * nb) \
-        + r256(4 * 4096 * 8)
+        + r256(4 * 65 * nb) + r256(4 * 4096 * 8) + r256(4 * 4096 * 8)
     assert L.ep_workspace_bytes(4096, 8, 256, 64) == want
     assert L.ep_workspace_bytes(0, 8, 256, 64) == 256
     for bad in [(-1, 2, 4, 2), (4, 0, 4, 2), (4, 2, 0, 1), (4, 2, 4, 0), (4, 2, 6, 4),
@@ -140,6 +140,31 @@ def test_layout_dispatch_rejects_bad_arguments(buf):
     for kw in [dict(x=None), dict(idx=None), dict(ce=None), dict(cp=None), dict(ip=None),
                dict(oe=None), dict(op=None), dict(rx=None), dict(src=None), dict(dst=None),
                dict(w=None), dict(H=0), dict(H=12), dict(dt=2), dict(dt=1, H=136),
+               dict(dt=1, rs=None), dict(E=6, P=4), dict(K=5), dict(T=-3),
+               dict(x=ctypes.c_void_p(0x100008)), dict(rx=ctypes.c_void_p(0x100004))]:
+        assert call(**kw) == INVALID, kw
+    assert call(E=2048, P=2) == UNSUPPORTED
+    assert call(wsz=128) == WORKSPACE
+
+
+def test_dispatch_dedup_rejects_bad_arguments(buf):
+    L = b.lib()
+    ws = buf(1 << 16)
+    args = {n: buf() for n in ["x", "idx", "ce", "cp", "ip", "oe", "op", "pto", "rx", "rs", "src",
+                               "rti", "ssr", "dst"]}
+
+    def call(T=4, H=256, K=2, E=4, P=2, dt=0, w=ws, wsz=1 << 16, **kw):
+        a = dict(args)
+        a.update(kw)
+        return L.ep_dispatch_dedup(a["x"], T, H, a["idx"], K, E, P, dt, a["ce"], a["cp"], a["ip"],
+                                   a["oe"], a["op"], a["pto"], a["rx"], a["rs"], a["src"],
+                                   a["rti"], a["ssr"], a["dst"], w, wsz, None)
+
+    for name in args:
+        if name == "rs":
+            continue
+        assert call(**{name: None}) == INVALID, name
+    for kw in [dict(w=None), dict(H=0), dict(H=12), dict(dt=2), dict(dt=1, H=136),
                dict(dt=1, rs=None), dict(E=6, P=4), dict(K=5), dict(T=-3),
                dict(x=ctypes.c_void_p(0x100008)), dict(rx=ctypes.c_void_p(0x100004))]:
         assert call(**kw) == INVALID, kw

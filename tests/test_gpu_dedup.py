@@ -1,0 +1,156 @@
+"""Parity of the de-duplicated per-partition dispatch with the CPU oracle (GPU).
+
+Each case runs ep_dispatch_dedup through the C ABI on cuda:0 and compares
+with the oracle's layout, permutation and de-duplicated layout on the same
+seeded inputs: the five layout outputs, partition token offsets, per-row
+source tokens and local expert ids, the slot-row map, dst_row and the
+invalid count bit for bit; the used receive rows (bf16 bits or E4M3 bytes and
+scales) bit for bit, and rows past the used ones untouched; and ep_combine on
+the returned dst_row within 2 bf16 ulp.  Cases: the five configurations at
+full size, ragged token blocks and channel chunks, masked, invalid and
+repeated ids, skew, P = 1, P = E, the largest E and K, one token, T = 0,
+everything routed to one expert, and a workspace shared with the other paths.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_ep_get_dispatch_amd import binding as ep
+from combine_ep_get_dispatch_amd import workloads as wl
+from parity import (MAX_COMBINE_ULP, announce, bf16_bits, compare, run_gpu, run_oracle,
+                    to_dev_bf16, ulp_distance)
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL_BF16 = 0x7FBF
+SENTINEL_FP8 = 0x7F
+
+
+def check_dedup(case, label, workspace=None, with_combine=True):
+    T, K, E, P, H = case.T, case.K, case.E, case.P, case.H
+    Kp = min(K, P)
+    RD = T * Kp
+    announce("dedup %s T=%d H=%d E=%d P=%d K=%d fp8=%s" % (label, T, H, E, P, K, case.fp8))
+    dev = torch.device("cuda:0")
+    idx = torch.from_numpy(np.ascontiguousarray(case.topk_idx)).to(dev)
+    x = to_dev_bf16(case.x_bits)
+    if case.fp8:
+        rx = torch.full((RD, H), SENTINEL_FP8, dtype=torch.uint8, device=dev)
+        rs = torch.full((RD, H // 128), -1.0, dtype=torch.float32, device=dev)
+    else:
+        rx = torch.full((RD, H), SENTINEL_BF16, dtype=torch.int16, device=dev).view(torch.bfloat16)
+        rs = None
+    out = ep.DedupDispatched(torch.full((P + 1,), -7, dtype=torch.int32, device=dev), rx, rs,
+                             torch.full((RD,), -7, dtype=torch.int32, device=dev),
+                             torch.full((RD, K), -7, dtype=torch.int32, device=dev),
+                             torch.full((T * K,), -7, dtype=torch.int32, device=dev),
+                             torch.full((T, K), -7, dtype=torch.int32, device=dev))
+    lay, d = ep.dispatch_dedup(x, idx, E, P, workspace=workspace, fp8=case.fp8, out=out)
+    if with_combine:
+        y = to_dev_bf16(case.y_bits)
+        w = torch.from_numpy(case.topk_weights).to(dev)
+        comb = bf16_bits(ep.combine(y, d.dst_row, w))
+    nerr = ep.get_device_error(lay.workspace)
+    torch.cuda.synchronize()
+
+    o = oracle.dedup_layout(case.topk_idx, E, P)
+    for key, got in [("num_tokens_per_expert", lay.num_tokens_per_expert),
+                     ("num_tokens_per_partition", lay.num_tokens_per_partition),
+                     ("is_token_in_partition", lay.is_token_in_partition),
+                     ("expert_offsets", lay.expert_offsets),
+                     ("partition_offsets", lay.partition_offsets),
+                     ("partition_token_offsets", d.partition_token_offsets),
+                     ("dedup_src_token", d.recv_src_token),
+                     ("dedup_topk_idx", d.recv_topk_idx),
+                     ("slot_src_row", d.slot_src_row),
+                     ("dst_row", d.dst_row)]:
+        np.testing.assert_array_equal(got.cpu().numpy(), np.asarray(o[key]), err_msg=key)
+    assert nerr == o["num_invalid"]
+    ND = o["num_dedup_rows"]
+    src = o["dedup_src_token"]
+    if case.fp8:
+        want_x, want_s = oracle.dispatch_rows_fp8(case.x_bits, src, fill=SENTINEL_FP8)
+        got_s = d.recv_scales.cpu().numpy()
+        np.testing.assert_array_equal(d.recv_x.cpu().numpy(), want_x, err_msg="recv_x")
+        np.testing.assert_array_equal(got_s[:ND].view(np.uint32), want_s[:ND].view(np.uint32),
+                                      err_msg="recv_scales")
+        assert np.all(got_s[ND:] == -1.0), "rows past the used ones were written"
+    else:
+        want_x = oracle.dispatch_rows_bf16(case.x_bits, src, fill=SENTINEL_BF16)
+        np.testing.assert_array_equal(bf16_bits(d.recv_x), want_x, err_msg="recv_x")
+    stats = dict(rows=ND, copies_per_token=round(ND / max(T, 1), 3))
+    if with_combine:
+        want = oracle.combine(case.y_bits, o["dst_row"], case.topk_weights)
+        u = ulp_distance(comb, want)
+        stats["combine_max_ulp"] = int(u.max(initial=0))
+        assert stats["combine_max_ulp"] <= MAX_COMBINE_ULP
+    announce("dedup %s ok %s" % (label, stats))
+    return stats
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skewed", "coarse"])
+def test_configuration_full_size(name):
+    case = wl.make(name)
+    stats = check_dedup(case, "config " + name)
+    if name == "prefill":
+        assert stats["copies_per_token"] < 8.0
+
+
+CASES = [
+    # T, H, E, P, K, seed, kwargs
+    (1000, 264, 16, 4, 3, 51, dict()),
+    (777, 1032, 64, 8, 6, 52, dict(masked_frac=0.1)),
+    (513, 384, 32, 4, 4, 53, dict(fp8=True)),
+    (300, 1152, 256, 64, 8, 54, dict(fp8=True, masked_frac=0.05)),
+    (2500, 520, 8, 8, 2, 55, dict(skew=2.0)),
+    (130, 136, 12, 3, 5, 57, dict(allow_dup=True)),
+    (257, 2048, 128, 16, 16, 58, dict(fp8=True)),
+    (65, 512, 40, 5, 7, 59, dict(masked_frac=0.3, invalid_frac=0.1)),
+    (4097, 128, 1024, 1024, 64, 60, dict()),
+    (1, 8, 4, 2, 2, 61, dict()),
+    (50, 256, 1, 1, 1, 62, dict()),
+    (200, 640, 16, 1, 16, 63, dict(fp8=True)),
+    (100_000, 16, 4, 2, 1, 64, dict()),
+    (9000, 128, 256, 64, 8, 65, dict(masked_frac=0.02, invalid_frac=0.01)),
+]
+
+
+@pytest.mark.parametrize("T,H,E,P,K,seed,kw", CASES,
+                         ids=["T%d_H%d_E%d_P%d_K%d" % c[:5] for c in CASES])
+def test_generic_case(T, H, E, P, K, seed, kw):
+    case = wl.random_case(T, H, E, P, K, seed, **kw)
+    check_dedup(case, "random seed=%d" % seed)
+
+
+def test_all_tokens_to_one_expert():
+    case = wl.random_case(5000, 256, 32, 8, 2, 66)
+    case.topk_idx[:] = 17
+    stats = check_dedup(case, "one hot expert")
+    assert stats["rows"] == 5000
+
+
+def test_zero_tokens():
+    announce("dedup zero tokens")
+    dev = torch.device("cuda:0")
+    idx = torch.zeros((0, 4), dtype=torch.int64, device=dev)
+    x = torch.zeros((0, 256), dtype=torch.bfloat16, device=dev)
+    lay, d = ep.dispatch_dedup(x, idx, 16, 4, fp8=True)
+    torch.cuda.synchronize()
+    assert d.partition_token_offsets.cpu().tolist() == [0] * 5
+    assert lay.expert_offsets.cpu().tolist() == [0] * 17
+    assert ep.get_device_error(lay.workspace) == 0
+
+
+def test_workspace_shared_with_other_paths():
+    big = wl.random_case(5000, 256, 64, 16, 8, 67, invalid_frac=0.01, with_y=True)
+    small = wl.random_case(600, 512, 16, 4, 4, 68, fp8=True)
+    ws = ep.new_workspace(5000, 8, 64, 16)
+    for case, how in [(big, "dedup"), (big, "two"), (small, "dedup"), (big, "one"),
+                      (big, "dedup"), (small, "two")]:
+        announce("shared workspace T=%d %s" % (case.T, how))
+        if how == "dedup":
+            check_dedup(case, "shared workspace", workspace=ws, with_combine=False)
+        else:
+            g = run_gpu(case, workspace=ws, one_call=(how == "one"))
+            compare(g, run_oracle(case), case)
