@@ -176,6 +176,10 @@ def main():
                     help="steps captured back to back in the one graph (--graph)")
     ap.add_argument("--two-calls", action="store_true",
                     help="layout and dispatch as two calls instead of ep_layout_dispatch")
+    ap.add_argument("--cu-budget", type=int, default=0,
+                    help="confine dispatch and combine to this many CUs (one-call path)")
+    ap.add_argument("--overlap-gemm", action="store_true",
+                    help="also time the step beside a bf16 GEMM on a second stream")
     ap.add_argument("--dedup", action="store_true",
                     help="time ep_dispatch_dedup (one copy per token and partition) + combine")
     ap.add_argument("--low-latency", action="store_true",
@@ -259,8 +263,10 @@ def main():
                      ("dispatch", lambda: ep.dispatch(x, idx, E, P, ws, fp8=fp8, out=disp))]
         else:
             calls = [("layout_dispatch", lambda: ep.layout_dispatch(
-                x, idx, E, P, workspace=ws, fp8=fp8, out_layout=lay, out=disp))]
-        calls.append(("combine", lambda: ep.combine(y, disp.dst_row, w, out=out)))
+                x, idx, E, P, workspace=ws, fp8=fp8, out_layout=lay, out=disp,
+                num_cus=args.cu_budget))]
+        calls.append(("combine", lambda: ep.combine(y, disp.dst_row, w, out=out,
+                                                    num_cus=args.cu_budget)))
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -351,6 +357,52 @@ def main():
         nb = algorithmic_bytes(T, H, E, P, K, fp8)
     value = nb["total"] / (ms_per_step * 1e-3) / 1e9
 
+    # ---- the step beside a GEMM on another stream (CU budget use case) ------
+    overlap = None
+    if args.overlap_gemm:
+        ga = torch.randn((4096, 7168), dtype=torch.bfloat16, device=dev)
+        gb = torch.randn((7168, 2048), dtype=torch.bfloat16, device=dev)
+        gc = torch.empty((4096, 2048), dtype=torch.bfloat16, device=dev)
+        gs = torch.cuda.Stream()           # default priority
+        n_ov = max(5, args.steps // 2)
+
+        def gemms():
+            for _ in range(n_ov):
+                torch.matmul(ga, gb, out=gc)
+
+        def steps():
+            for _ in range(n_ov):
+                step()
+
+        def timed(run_steps, run_gemms):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e2 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            gs.wait_event(e0)
+            if run_gemms:
+                with torch.cuda.stream(gs):
+                    gemms()
+            if run_steps:
+                steps()
+            e1.record()
+            e2.record(gs)
+            torch.cuda.synchronize()
+            return max(e0.elapsed_time(e1), e0.elapsed_time(e2)) * 1e3 / n_ov
+
+        timed(True, True)                  # warm-up
+        g_us = timed(False, True)
+        s_us = timed(True, False)
+        b_us = timed(True, True)
+        overlap = {"gemm": "bf16 4096x7168 @ 7168x2048 (torch.matmul) on a second stream",
+                   "cu_budget": args.cu_budget, "pairs": n_ov,
+                   "gemm_us": round(g_us, 2), "step_us": round(s_us, 2),
+                   "both_us": round(b_us, 2),
+                   "sequential_over_concurrent": round((g_us + s_us) / b_us, 3)}
+        log("overlap: gemm %.1f us, step %.1f us, both %.1f us per pair" % (g_us, s_us, b_us))
+        del ga, gb, gc
+
     # ---- copy ceiling (measured) ---------------------------------------------
     copy_gbs = None
     if not args.no_copy_ceiling:
@@ -422,6 +474,7 @@ def main():
                                                   % C if args.low_latency else ""),
                    "tokens": T, "hidden": H, "experts": E, "partitions": P, "topk": K,
                    "fp8_dispatch": fp8, "parallelism": "single GPU",
+                   "cu_budget": args.cu_budget or None,
                    "path": "low_latency" if args.low_latency else
                            ("de-duplicated per partition" if args.dedup else
                             ("offsets, two calls" if args.two_calls else "offsets, one call"))},
@@ -432,6 +485,7 @@ def main():
         "pct_of_copy_ceiling": round(100 * value / copy_gbs, 2) if copy_gbs else None,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "overlap": overlap,
         "device": torch.cuda.get_device_name(dev),
     }
     print(json.dumps(result), flush=True)

@@ -45,6 +45,10 @@ SIGNATURES = {
     "ep_dispatch": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _i32, ctypes.c_int, _vp,
                                    _vp, _vp, _vp, _vp, _sz, _vp]),
     "ep_combine": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "ep_combine_cu": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp]),
+    "ep_layout_dispatch_cu": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _i32, ctypes.c_int,
+                                             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                             _sz, _i32, _vp]),
     "ep_layout_dispatch": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _i32, ctypes.c_int,
                                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                           _vp]),
@@ -226,9 +230,11 @@ def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_part
 def layout_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int,
                     num_partitions: int, workspace: torch.Tensor | None = None,
                     fp8: bool = False, out_layout: Layout | None = None,
-                    out: Dispatched | None = None):
+                    out: Dispatched | None = None, num_cus: int = 0):
     """ep_layout_dispatch: the outputs of get_dispatch_layout + dispatch from
-    one call (one kernel launch fewer).  Returns (Layout, Dispatched)."""
+    one call (one kernel launch fewer).  num_cus > 0 confines the dispatch
+    launch to that many CUs (ep_layout_dispatch_cu).  Returns (Layout,
+    Dispatched)."""
     if x.dim() != 2 or topk_idx.dim() != 2:
         raise ValueError("x must be [T, H] and topk_idx [T, K]")
     T, H = x.shape
@@ -266,12 +272,13 @@ def layout_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int,
         _need(out.recv_scales, torch.float32, "recv_scales", (R, H // 128))
     _need(out.recv_src_token, torch.int32, "recv_src_token", (R,))
     _need(out.dst_row, torch.int32, "dst_row", (T, K))
-    _check(lib().ep_layout_dispatch(
+    _check(lib().ep_layout_dispatch_cu(
         _ptr(x), T, H, _ptr(topk_idx), K, E, P, EP_DTYPE_FP8_E4M3 if fp8 else EP_DTYPE_BF16,
         _ptr(lo.num_tokens_per_expert), _ptr(lo.num_tokens_per_partition),
         _ptr(lo.is_token_in_partition), _ptr(lo.expert_offsets), _ptr(lo.partition_offsets),
         _ptr(out.recv_x), _ptr(out.recv_scales) if fp8 else None, _ptr(out.recv_src_token),
-        _ptr(out.dst_row), _ptr(workspace), workspace.numel(), _stream(x)), "ep_layout_dispatch")
+        _ptr(out.dst_row), _ptr(workspace), workspace.numel(), int(num_cus), _stream(x)),
+        "ep_layout_dispatch_cu")
     return out_layout, out
 
 
@@ -395,8 +402,9 @@ def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: i
 
 
 def combine(y: torch.Tensor, dst_row: torch.Tensor, topk_weights: torch.Tensor,
-            out: torch.Tensor | None = None) -> torch.Tensor:
-    """ep_combine: y [R, H] bf16 expert outputs -> out [T, H] bf16."""
+            out: torch.Tensor | None = None, num_cus: int = 0) -> torch.Tensor:
+    """ep_combine: y [R, H] bf16 expert outputs -> out [T, H] bf16.  num_cus >
+    0 confines it to that many CUs (ep_combine_cu)."""
     if y.dim() != 2 or dst_row.dim() != 2:
         raise ValueError("y must be [R, H] and dst_row [T, K]")
     T, K = dst_row.shape
@@ -407,8 +415,8 @@ def combine(y: torch.Tensor, dst_row: torch.Tensor, topk_weights: torch.Tensor,
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
     _need(out, torch.bfloat16, "out", (T, H))
-    _check(lib().ep_combine(_ptr(y), y.shape[0], _ptr(dst_row), _ptr(topk_weights), T, K, H,
-                            _ptr(out), _stream(y)), "ep_combine")
+    _check(lib().ep_combine_cu(_ptr(y), y.shape[0], _ptr(dst_row), _ptr(topk_weights), T, K, H,
+                               _ptr(out), int(num_cus), _stream(y)), "ep_combine_cu")
     return out
 
 

@@ -74,18 +74,19 @@ ep_status_t ep_dispatch(const void* x, int32_t num_tokens, int32_t hidden,
     const ep::WsMap m = ep::ws_map(T, K, E, P);
     if (workspace_bytes < m.total) return EP_ERR_WORKSPACE;
     return from_hip(ep::launch_dispatch(static_cast<const uint16_t*>(x), T, H, K, fp8, recv_x,
-                                        recv_scales, recv_src_token, dst_row, workspace, m,
+                                        recv_scales, recv_src_token, dst_row, workspace, m, 0,
                                         static_cast<hipStream_t>(stream)));
 }
 
-ep_status_t ep_layout_dispatch(const void* x, int32_t num_tokens, int32_t hidden,
-                               const int64_t* topk_idx, int32_t num_topk, int32_t num_experts,
-                               int32_t num_partitions, ep_dtype_t out_dtype,
-                               int32_t* num_tokens_per_expert, int32_t* num_tokens_per_partition,
-                               uint8_t* is_token_in_partition, int32_t* expert_offsets,
-                               int32_t* partition_offsets, void* recv_x, float* recv_scales,
-                               int32_t* recv_src_token, int32_t* dst_row, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+ep_status_t ep_layout_dispatch_cu(const void* x, int32_t num_tokens, int32_t hidden,
+                                  const int64_t* topk_idx, int32_t num_topk, int32_t num_experts,
+                                  int32_t num_partitions, ep_dtype_t out_dtype,
+                                  int32_t* num_tokens_per_expert,
+                                  int32_t* num_tokens_per_partition,
+                                  uint8_t* is_token_in_partition, int32_t* expert_offsets,
+                                  int32_t* partition_offsets, void* recv_x, float* recv_scales,
+                                  int32_t* recv_src_token, int32_t* dst_row, void* workspace,
+                                  size_t workspace_bytes, int32_t num_cus, void* stream) {
     const int32_t T = num_tokens, H = hidden, K = num_topk, E = num_experts, P = num_partitions;
     ep_status_t st = check_routing_shape(T, K, E, P);
     if (st != EP_OK) return st;
@@ -101,13 +102,29 @@ ep_status_t ep_layout_dispatch(const void* x, int32_t num_tokens, int32_t hidden
         if (fp8 && !recv_scales) return EP_ERR_INVALID_ARG;
         if (!aligned16(x) || !aligned16(recv_x)) return EP_ERR_INVALID_ARG;
     }
+    if (num_cus < 0) return EP_ERR_INVALID_ARG;
     const ep::WsMap m = ep::ws_map(T, K, E, P);
     if (workspace_bytes < m.total) return EP_ERR_WORKSPACE;
     return from_hip(ep::launch_layout_dispatch(
         static_cast<const uint16_t*>(x), topk_idx, T, H, K, E, P, fp8, workspace, m,
         num_tokens_per_expert, num_tokens_per_partition, is_token_in_partition, expert_offsets,
-        partition_offsets, recv_x, recv_scales, recv_src_token, dst_row,
+        partition_offsets, recv_x, recv_scales, recv_src_token, dst_row, num_cus,
         static_cast<hipStream_t>(stream)));
+}
+
+ep_status_t ep_layout_dispatch(const void* x, int32_t num_tokens, int32_t hidden,
+                               const int64_t* topk_idx, int32_t num_topk, int32_t num_experts,
+                               int32_t num_partitions, ep_dtype_t out_dtype,
+                               int32_t* num_tokens_per_expert, int32_t* num_tokens_per_partition,
+                               uint8_t* is_token_in_partition, int32_t* expert_offsets,
+                               int32_t* partition_offsets, void* recv_x, float* recv_scales,
+                               int32_t* recv_src_token, int32_t* dst_row, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    return ep_layout_dispatch_cu(x, num_tokens, hidden, topk_idx, num_topk, num_experts,
+                                 num_partitions, out_dtype, num_tokens_per_expert,
+                                 num_tokens_per_partition, is_token_in_partition, expert_offsets,
+                                 partition_offsets, recv_x, recv_scales, recv_src_token, dst_row,
+                                 workspace, workspace_bytes, 0, stream);
 }
 
 ep_status_t ep_dispatch_dedup(const void* x, int32_t num_tokens, int32_t hidden,
@@ -170,11 +187,12 @@ ep_status_t ep_low_latency_dispatch(const void* x, int32_t num_tokens, int32_t h
         static_cast<hipStream_t>(stream)));
 }
 
-ep_status_t ep_combine(const void* y, int64_t num_rows, const int32_t* dst_row,
-                       const float* topk_weights, int32_t num_tokens, int32_t num_topk,
-                       int32_t hidden, void* out, void* stream) {
+ep_status_t ep_combine_cu(const void* y, int64_t num_rows, const int32_t* dst_row,
+                          const float* topk_weights, int32_t num_tokens, int32_t num_topk,
+                          int32_t hidden, void* out, int32_t num_cus, void* stream) {
     const int32_t T = num_tokens, K = num_topk, H = hidden;
-    if (T < 0 || K <= 0 || H <= 0 || H % 8 != 0 || num_rows < 0) return EP_ERR_INVALID_ARG;
+    if (T < 0 || K <= 0 || H <= 0 || H % 8 != 0 || num_rows < 0 || num_cus < 0)
+        return EP_ERR_INVALID_ARG;
     if ((int64_t)T * K >= kMaxRows) return EP_ERR_INVALID_ARG;
     if (K > EP_MAX_TOPK) return EP_ERR_UNSUPPORTED;
     if (T > 0) {
@@ -184,7 +202,14 @@ ep_status_t ep_combine(const void* y, int64_t num_rows, const int32_t* dst_row,
     if (T > 0 && num_rows > 0 && !y) return EP_ERR_INVALID_ARG;
     return from_hip(ep::launch_combine(static_cast<const uint16_t*>(y), num_rows, dst_row,
                                        topk_weights, T, K, H, static_cast<uint16_t*>(out),
-                                       static_cast<hipStream_t>(stream)));
+                                       num_cus, static_cast<hipStream_t>(stream)));
+}
+
+ep_status_t ep_combine(const void* y, int64_t num_rows, const int32_t* dst_row,
+                       const float* topk_weights, int32_t num_tokens, int32_t num_topk,
+                       int32_t hidden, void* out, void* stream) {
+    return ep_combine_cu(y, num_rows, dst_row, topk_weights, num_tokens, num_topk, hidden, out, 0,
+                         stream);
 }
 
 ep_status_t ep_get_device_error(const void* workspace, size_t workspace_bytes,

@@ -58,15 +58,14 @@ __device__ __forceinline__ void combine_slots(float (&acc)[8], const uint16_t* _
     }
 }
 
+// One wave's task: token t = task / nchunk, channel chunk task % nchunk.
 template <int KT>   // KT > 0: exactly KT slots; KT == 0: any K <= 64
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
-    const uint16_t* __restrict__ y, int64_t nrows, const int32_t* __restrict__ dst_row,
-    const float* __restrict__ w, int K, int H, uint16_t* __restrict__ out, int nchunk,
-    int64_t ntask) {
+__device__ __forceinline__ void combine_task(const uint16_t* __restrict__ y, int64_t nrows,
+                                             const int32_t* __restrict__ dst_row,
+                                             const float* __restrict__ w, int K, int H,
+                                             uint16_t* __restrict__ out, int nchunk,
+                                             int64_t task) {
     const int lane = threadIdx.x & 63;
-    const int64_t task = (int64_t)blockIdx.x * (kCombineThreads / 64) +
-                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (task >= ntask) return;
     const int t = (int)(task / nchunk);
     const int c = (int)(task - (int64_t)t * nchunk);
     const int h0 = c * kCombineChunk + lane * 8;
@@ -99,29 +98,65 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 }
 
 template <int KT>
-void launch_k(dim3 grid, hipStream_t s, const uint16_t* y, int64_t nrows,
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+    const uint16_t* __restrict__ y, int64_t nrows, const int32_t* __restrict__ dst_row,
+    const float* __restrict__ w, int K, int H, uint16_t* __restrict__ out, int nchunk,
+    int64_t ntask) {
+    const int64_t task = (int64_t)blockIdx.x * (kCombineThreads / 64) +
+                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (task >= ntask) return;
+    combine_task<KT>(y, nrows, dst_row, w, K, H, out, nchunk, task);
+}
+
+// CU-budget form: a grid of at most num_cus workgroups of kBudgetThreads,
+// every wave striding over the tasks, so the hardware places the work on at
+// most num_cus CUs and leaves the others to concurrent kernels.
+template <int KT>
+__global__ __launch_bounds__(kBudgetThreads) void combine_budget_kernel(
+    const uint16_t* __restrict__ y, int64_t nrows, const int32_t* __restrict__ dst_row,
+    const float* __restrict__ w, int K, int H, uint16_t* __restrict__ out, int nchunk,
+    int64_t ntask) {
+    const int wpb = kBudgetThreads / 64;
+    for (int64_t task = (int64_t)blockIdx.x * wpb + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+         task < ntask; task += (int64_t)gridDim.x * wpb)
+        combine_task<KT>(y, nrows, dst_row, w, K, H, out, nchunk, task);
+}
+
+template <int KT>
+void launch_k(dim3 grid, bool budget, hipStream_t s, const uint16_t* y, int64_t nrows,
               const int32_t* dst_row, const float* w, int K, int H, uint16_t* out, int nchunk,
               int64_t ntask) {
-    hipLaunchKernelGGL(combine_kernel<KT>, grid, dim3(kCombineThreads), 0, s, y, nrows, dst_row,
-                       w, K, H, out, nchunk, ntask);
+    if (budget)
+        hipLaunchKernelGGL(combine_budget_kernel<KT>, grid, dim3(kBudgetThreads), 0, s, y, nrows,
+                           dst_row, w, K, H, out, nchunk, ntask);
+    else
+        hipLaunchKernelGGL(combine_kernel<KT>, grid, dim3(kCombineThreads), 0, s, y, nrows,
+                           dst_row, w, K, H, out, nchunk, ntask);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const uint16_t* y, int64_t nrows, const int32_t* dst_row,
-                          const float* w, int T, int K, int H, uint16_t* out, hipStream_t s) {
+                          const float* w, int T, int K, int H, uint16_t* out, int num_cus,
+                          hipStream_t s) {
     if (T == 0) return hipSuccess;
     const int nchunk = (H + kCombineChunk - 1) / kCombineChunk;
     const int64_t ntask = (int64_t)T * nchunk;
-    const int wpb = kCombineThreads / 64;
-    const dim3 grid((unsigned)((ntask + wpb - 1) / wpb));
+    int64_t nblk = (ntask + kCombineThreads / 64 - 1) / (kCombineThreads / 64);
+    bool budget = false;
+    if (num_cus > 0) {
+        const int64_t bblk = (ntask + kBudgetThreads / 64 - 1) / (kBudgetThreads / 64);
+        budget = true;
+        nblk = bblk < num_cus ? bblk : num_cus;
+    }
+    const dim3 grid((unsigned)nblk);
     switch (K) {
-        case 1: launch_k<1>(grid, s, y, nrows, dst_row, w, K, H, out, nchunk, ntask); break;
-        case 2: launch_k<2>(grid, s, y, nrows, dst_row, w, K, H, out, nchunk, ntask); break;
-        case 4: launch_k<4>(grid, s, y, nrows, dst_row, w, K, H, out, nchunk, ntask); break;
-        case 6: launch_k<6>(grid, s, y, nrows, dst_row, w, K, H, out, nchunk, ntask); break;
-        case 8: launch_k<8>(grid, s, y, nrows, dst_row, w, K, H, out, nchunk, ntask); break;
-        default: launch_k<0>(grid, s, y, nrows, dst_row, w, K, H, out, nchunk, ntask); break;
+        case 1: launch_k<1>(grid, budget, s, y, nrows, dst_row, w, K, H, out, nchunk, ntask); break;
+        case 2: launch_k<2>(grid, budget, s, y, nrows, dst_row, w, K, H, out, nchunk, ntask); break;
+        case 4: launch_k<4>(grid, budget, s, y, nrows, dst_row, w, K, H, out, nchunk, ntask); break;
+        case 6: launch_k<6>(grid, budget, s, y, nrows, dst_row, w, K, H, out, nchunk, ntask); break;
+        case 8: launch_k<8>(grid, budget, s, y, nrows, dst_row, w, K, H, out, nchunk, ntask); break;
+        default: launch_k<0>(grid, budget, s, y, nrows, dst_row, w, K, H, out, nchunk, ntask); break;
     }
     return hipGetLastError();
 }

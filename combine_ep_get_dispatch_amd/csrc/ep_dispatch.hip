@@ -168,14 +168,13 @@ __device__ __forceinline__ void scatter_token(const uint16_t* __restrict__ x, in
 }
 
 template <bool FP8>
-__global__ __launch_bounds__(kDispatchMaxThreads) void dispatch_kernel(
-    const uint16_t* __restrict__ x, int H, int K, const WsHeader* __restrict__ hdr,
+__device__ __forceinline__ void dispatch_token(
+    int t, const uint16_t* __restrict__ x, int H, int K, const WsHeader* __restrict__ hdr,
     const int* __restrict__ rows, void* __restrict__ recv_x, float* __restrict__ recv_scales,
-    int32_t* __restrict__ recv_src, int32_t* __restrict__ dst_row, int nchunk, int nrows) {
-    extern __shared__ float s_scale[];   // [G] scales of this token (FP8)
+    int32_t* __restrict__ recv_src, int32_t* __restrict__ dst_row, int nchunk, int nrows,
+    float* s_scale) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int t = blockIdx.x;
 
     // Destination row of slot k = lane (K <= 64).  (Loading x before these
     // rows are known measured slower, here and in the decode kernel.)
@@ -196,6 +195,26 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void dispatch_kernel(
     scatter_token<FP8>(x, H, K, t, drow, first, recv_x, recv_scales, s_scale, nchunk);
 }
 
+// One workgroup per token, or (LOOP, the CU-budget form) a smaller grid whose
+// workgroups take tokens blockIdx.x, blockIdx.x + gridDim.x, ...
+template <bool FP8, bool LOOP>
+__global__ __launch_bounds__(kDispatchMaxThreads) void dispatch_kernel(
+    const uint16_t* __restrict__ x, int T, int H, int K, const WsHeader* __restrict__ hdr,
+    const int* __restrict__ rows, void* __restrict__ recv_x, float* __restrict__ recv_scales,
+    int32_t* __restrict__ recv_src, int32_t* __restrict__ dst_row, int nchunk, int nrows) {
+    extern __shared__ float s_scale[];   // [G] scales of this token (FP8)
+    if constexpr (!LOOP) {
+        dispatch_token<FP8>(blockIdx.x, x, H, K, hdr, rows, recv_x, recv_scales, recv_src,
+                            dst_row, nchunk, nrows, s_scale);
+    } else {
+        for (int t = blockIdx.x; t < T; t += gridDim.x) {
+            dispatch_token<FP8>(t, x, H, K, hdr, rows, recv_x, recv_scales, recv_src, dst_row,
+                                nchunk, nrows, s_scale);
+            __syncthreads();               // the next token reuses the LDS
+        }
+    }
+}
+
 // Dispatch that also finishes the layout (after the count launch in kCountPre mode).
 // Slot (t,k) of expert e, in token block b, with rank r inside the block:
 //   row = expert_offsets[e] + (rows of e in blocks < b) + r
@@ -205,23 +224,21 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void dispatch_kernel(
 // for it (k = K: block j's term of N): one round of L2 loads after the row
 // load, spread over (K+1)*S threads.  A shuffle reduction over each S-lane
 // segment gives the row, which reaches the other waves through LDS (one
-// barrier).  Workgroup 0 also writes the counts, offsets and header.
+// barrier).  The workgroup handling token 0 also writes the counts, offsets
+// and header.  s_scale ([G]), s_row ([64]) and s_n are the workgroup's LDS.
 template <bool FP8>
-__global__ __launch_bounds__(kDispatchMaxThreads) void layout_dispatch_kernel(
-    const uint16_t* __restrict__ x, int H, int K, int E, int P, int Ep, int TB, int nb,
+__device__ __forceinline__ void layout_dispatch_token(
+    int t, const uint16_t* __restrict__ x, int H, int K, int E, int P, int Ep, int TB, int nb,
     int seg_log2, const int* __restrict__ cnt, const int* __restrict__ pre,
     const int* __restrict__ pcnt, const int* __restrict__ inv, const int* __restrict__ rows,
     WsHeader* __restrict__ hdr, int32_t* __restrict__ cnt_e, int32_t* __restrict__ cnt_p,
     int32_t* __restrict__ off_e, int32_t* __restrict__ off_p, void* __restrict__ recv_x,
     float* __restrict__ recv_scales, int32_t* __restrict__ recv_src,
-    int32_t* __restrict__ dst_row, int nchunk, int nrows) {
-    extern __shared__ float s_scale[];   // [G] scales of this token (FP8)
-    __shared__ int s_row[64];            // receive row of slot k (K <= 64)
-    __shared__ int s_n;                  // N
+    int32_t* __restrict__ dst_row, int nchunk, int nrows, float* s_scale, int* s_row,
+    int& s_n) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int t = blockIdx.x;
 
     {
         const int b = t / TB;
@@ -286,6 +303,36 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void layout_dispatch_kernel(
     ChunkData first;
     if (wave < nchunk) first = load_chunk<FP8>(x, H, t, wave, s_scale);
     scatter_token<FP8>(x, H, K, t, drow, first, recv_x, recv_scales, s_scale, nchunk);
+}
+
+// One workgroup per token, or (LOOP, the CU-budget form) a smaller grid whose
+// workgroups take tokens blockIdx.x, blockIdx.x + gridDim.x, ...
+template <bool FP8, bool LOOP>
+__global__ __launch_bounds__(kDispatchMaxThreads) void layout_dispatch_kernel(
+    const uint16_t* __restrict__ x, int T, int H, int K, int E, int P, int Ep, int TB, int nb,
+    int seg_log2, const int* __restrict__ cnt, const int* __restrict__ pre,
+    const int* __restrict__ pcnt, const int* __restrict__ inv, const int* __restrict__ rows,
+    WsHeader* __restrict__ hdr, int32_t* __restrict__ cnt_e, int32_t* __restrict__ cnt_p,
+    int32_t* __restrict__ off_e, int32_t* __restrict__ off_p, void* __restrict__ recv_x,
+    float* __restrict__ recv_scales, int32_t* __restrict__ recv_src,
+    int32_t* __restrict__ dst_row, int nchunk, int nrows) {
+    extern __shared__ float s_scale[];   // [G] scales of this token (FP8)
+    __shared__ int s_row[64];            // receive row of slot k (K <= 64)
+    __shared__ int s_n;                  // N
+    if constexpr (!LOOP) {
+        layout_dispatch_token<FP8>(blockIdx.x, x, H, K, E, P, Ep, TB, nb, seg_log2, cnt, pre,
+                                   pcnt, inv, rows, hdr, cnt_e, cnt_p, off_e, off_p, recv_x,
+                                   recv_scales, recv_src, dst_row, nchunk, nrows, s_scale, s_row,
+                                   s_n);
+    } else {
+        for (int t = blockIdx.x; t < T; t += gridDim.x) {
+            layout_dispatch_token<FP8>(t, x, H, K, E, P, Ep, TB, nb, seg_log2, cnt, pre, pcnt,
+                                       inv, rows, hdr, cnt_e, cnt_p, off_e, off_p, recv_x,
+                                       recv_scales, recv_src, dst_row, nchunk, nrows, s_scale,
+                                       s_row, s_n);
+            __syncthreads();               // the next token reuses the LDS
+        }
+    }
 }
 
 // De-duplicated per-partition dispatch (after the count launch in kCountDedup
@@ -575,7 +622,7 @@ __global__ void ll_empty_kernel(int E, int C, int32_t* __restrict__ cnt_e,
 
 hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K, bool fp8, void* recv_x,
                            float* recv_scales, int32_t* recv_src, int32_t* dst_row,
-                           const void* ws, const WsMap& m, hipStream_t s) {
+                           const void* ws, const WsMap& m, int num_cus, hipStream_t s) {
     if (T == 0) return hipSuccess;
     const char* base = static_cast<const char*>(ws);
     const WsHeader* hdr = reinterpret_cast<const WsHeader*>(base);
@@ -583,12 +630,18 @@ hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K, bool fp8, voi
     const int nchunk = (H + kDispatchChunk - 1) / kDispatchChunk;
     const int nw = nchunk < kDispatchMaxThreads / 64 ? nchunk : kDispatchMaxThreads / 64;
     const size_t lds = fp8 ? sizeof(float) * (size_t)(H / 128) : 0;
-    if (fp8)
-        hipLaunchKernelGGL(dispatch_kernel<true>, dim3(T), dim3(64 * nw), lds, s, x, H, K, hdr,
-                           rows, recv_x, recv_scales, recv_src, dst_row, nchunk, T * K);
+    const bool loop = num_cus > 0 && num_cus < T;
+    const dim3 grid(loop ? (unsigned)num_cus : (unsigned)T);
+#define EP_D_ARGS x, T, H, K, hdr, rows, recv_x, recv_scales, recv_src, dst_row, nchunk, T * K
+    if (fp8 && loop)
+        hipLaunchKernelGGL((dispatch_kernel<true, true>), grid, dim3(64 * nw), lds, s, EP_D_ARGS);
+    else if (fp8)
+        hipLaunchKernelGGL((dispatch_kernel<true, false>), grid, dim3(64 * nw), lds, s, EP_D_ARGS);
+    else if (loop)
+        hipLaunchKernelGGL((dispatch_kernel<false, true>), grid, dim3(64 * nw), 0, s, EP_D_ARGS);
     else
-        hipLaunchKernelGGL(dispatch_kernel<false>, dim3(T), dim3(64 * nw), 0, s, x, H, K, hdr,
-                           rows, recv_x, recv_scales, recv_src, dst_row, nchunk, T * K);
+        hipLaunchKernelGGL((dispatch_kernel<false, false>), grid, dim3(64 * nw), 0, s, EP_D_ARGS);
+#undef EP_D_ARGS
     return hipGetLastError();
 }
 
@@ -627,7 +680,7 @@ hipError_t launch_layout_dispatch(const uint16_t* x, const int64_t* idx, int T, 
                                   int32_t* cnt_e, int32_t* cnt_p, uint8_t* in_part,
                                   int32_t* off_e, int32_t* off_p, void* recv_x,
                                   float* recv_scales, int32_t* recv_src, int32_t* dst_row,
-                                  hipStream_t s) {
+                                  int num_cus, hipStream_t s) {
     const int nchunk = (H + kDispatchChunk - 1) / kDispatchChunk;
     const int nw = nchunk < kDispatchMaxThreads / 64 ? nchunk : kDispatchMaxThreads / 64;
     // The finishing sums are one round of loads per token workgroup and a
@@ -642,7 +695,8 @@ hipError_t launch_layout_dispatch(const uint16_t* x, const int64_t* idx, int T, 
         hipError_t e = launch_layout(idx, T, K, E, P, ws, m, cnt_e, cnt_p, in_part, off_e, off_p,
                                      s);
         if (e != hipSuccess) return e;
-        return launch_dispatch(x, T, H, K, fp8, recv_x, recv_scales, recv_src, dst_row, ws, m, s);
+        return launch_dispatch(x, T, H, K, fp8, recv_x, recv_scales, recv_src, dst_row, ws, m,
+                               num_cus, s);
     }
     hipError_t e = launch_layout_count(idx, T, K, E, P, ws, m, in_part, kCountPre, s);
     if (e != hipSuccess) return e;
@@ -654,16 +708,23 @@ hipError_t launch_layout_dispatch(const uint16_t* x, const int64_t* idx, int T, 
     const int* pre = reinterpret_cast<const int*>(base + m.pre_off);
     const int* rows = reinterpret_cast<const int*>(base + m.rows_off);
     const size_t lds = fp8 ? sizeof(float) * (size_t)(H / 128) : 0;
-    if (fp8)
-        hipLaunchKernelGGL(layout_dispatch_kernel<true>, dim3(T), dim3(64 * nw), lds, s, x, H, K,
-                           E, P, E / P, m.tb, m.nb, seg_log2, cnt, pre, pcnt, inv, rows, hdr,
-                           cnt_e, cnt_p, off_e, off_p, recv_x, recv_scales, recv_src, dst_row,
-                           nchunk, T * K);
+    const bool loop = num_cus > 0 && num_cus < T;
+    const dim3 grid(loop ? (unsigned)num_cus : (unsigned)T);
+#define EP_LD_ARGS x, T, H, K, E, P, E / P, m.tb, m.nb, seg_log2, cnt, pre, pcnt, inv, rows, hdr, \
+                   cnt_e, cnt_p, off_e, off_p, recv_x, recv_scales, recv_src, dst_row, nchunk, T * K
+    if (fp8 && loop)
+        hipLaunchKernelGGL((layout_dispatch_kernel<true, true>), grid, dim3(64 * nw), lds, s,
+                           EP_LD_ARGS);
+    else if (fp8)
+        hipLaunchKernelGGL((layout_dispatch_kernel<true, false>), grid, dim3(64 * nw), lds, s,
+                           EP_LD_ARGS);
+    else if (loop)
+        hipLaunchKernelGGL((layout_dispatch_kernel<false, true>), grid, dim3(64 * nw), lds, s,
+                           EP_LD_ARGS);
     else
-        hipLaunchKernelGGL(layout_dispatch_kernel<false>, dim3(T), dim3(64 * nw), lds, s, x, H, K,
-                           E, P, E / P, m.tb, m.nb, seg_log2, cnt, pre, pcnt, inv, rows, hdr,
-                           cnt_e, cnt_p, off_e, off_p, recv_x, recv_scales, recv_src, dst_row,
-                           nchunk, T * K);
+        hipLaunchKernelGGL((layout_dispatch_kernel<false, false>), grid, dim3(64 * nw), lds, s,
+                           EP_LD_ARGS);
+#undef EP_LD_ARGS
     return hipGetLastError();
 }
 

@@ -8,6 +8,11 @@
 
 namespace ep {
 
+// CU budget: the *_cu entry points launch at most num_cus workgroups of this
+// size (or the kernel's own size) that loop over their work, so that the
+// hardware places them on at most num_cus CUs.
+constexpr int kBudgetThreads = 1024;
+
 // ---------------------------------------------------------------- layout ---
 // The layout kernel gives each workgroup one block of consecutive tokens
 // holding about kLayoutEntries (token, slot) entries, split over 8 waves.
@@ -108,9 +113,11 @@ hipError_t launch_layout_count(const int64_t* idx, int T, int K, int E, int P, v
 constexpr int kDispatchMaxThreads = 1024;
 constexpr int kDispatchChunk = 1024;
 
+// num_cus > 0 (and < T): the CU-budget form, num_cus workgroups looping over
+// the tokens; otherwise one workgroup per token.
 hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K, bool fp8, void* recv_x,
                            float* recv_scales, int32_t* recv_src, int32_t* dst_row,
-                           const void* ws, const WsMap& m, hipStream_t s);
+                           const void* ws, const WsMap& m, int num_cus, hipStream_t s);
 
 // Largest (E + 1) * blocks that workgroup 0 of the one-call layout + dispatch
 // sums (beyond it the call takes the two-step form).
@@ -128,7 +135,7 @@ hipError_t launch_layout_dispatch(const uint16_t* x, const int64_t* idx, int T, 
                                   int32_t* cnt_e, int32_t* cnt_p, uint8_t* in_part,
                                   int32_t* off_e, int32_t* off_p, void* recv_x,
                                   float* recv_scales, int32_t* recv_src, int32_t* dst_row,
-                                  hipStream_t s);
+                                  int num_cus, hipStream_t s);
 
 // Fixed-capacity (decode) dispatch: one launch, one workgroup per token (T = 0
 // takes a small fill kernel instead) of kLlWaves waves, so that the routing scan every
@@ -163,8 +170,11 @@ hipError_t launch_dispatch_dedup(const uint16_t* x, const int64_t* idx, int T, i
 constexpr int kCombineThreads = 128;
 constexpr int kCombineChunk = 512;
 
+// num_cus > 0: the CU-budget form (at most num_cus workgroups of
+// kBudgetThreads striding over the tasks); otherwise the ordinary launch.
 hipError_t launch_combine(const uint16_t* y, int64_t nrows, const int32_t* dst_row,
-                          const float* w, int T, int K, int H, uint16_t* out, hipStream_t s);
+                          const float* w, int T, int K, int H, uint16_t* out, int num_cus,
+                          hipStream_t s);
 
 // ------------------------------------------------------------ diagnostics ---
 hipError_t launch_convert_e4m3(const float* in, uint8_t* out, int64_t n, int mode, hipStream_t s);

@@ -253,6 +253,35 @@ ep_status_t ep_low_latency_dispatch(const void *x, int32_t num_tokens, int32_t h
                                     int32_t *dst_row, int64_t *num_invalid, void *stream);
 
 /*
+ * CU budget: ep_layout_dispatch and ep_combine confined to at most num_cus
+ * compute units, so that they can run beside other kernels (expert GEMMs)
+ * on the same GPU -- the pages' "flexible GPU resource control" for
+ * overlapping communication with computation ("DeepSeek releases DeepEP, an
+ * efficient communication library for MoE models", feature list; users
+ * choose the number of SMs the kernels use, "Deepseek Ai Deepep: A library
+ * for an open-open EP for example training", section "Technological Views
+ * and Benefits").  The dispatch launch (and combine) then runs as at most
+ * num_cus workgroups that loop over the tokens (tasks); the hardware places
+ * them on at most num_cus CUs.  Results are identical to the calls without
+ * a budget; num_cus = 0 means no budget; num_cus < 0 is EP_ERR_INVALID_ARG.
+ * The count launch of ep_layout_dispatch_cu already uses only
+ * ceil(T / (2048 / K)) workgroups.
+ */
+ep_status_t ep_layout_dispatch_cu(const void *x, int32_t num_tokens, int32_t hidden,
+                                  const int64_t *topk_idx, int32_t num_topk, int32_t num_experts,
+                                  int32_t num_partitions, ep_dtype_t out_dtype,
+                                  int32_t *num_tokens_per_expert,
+                                  int32_t *num_tokens_per_partition,
+                                  uint8_t *is_token_in_partition, int32_t *expert_offsets,
+                                  int32_t *partition_offsets, void *recv_x, float *recv_scales,
+                                  int32_t *recv_src_token, int32_t *dst_row, void *workspace,
+                                  size_t workspace_bytes, int32_t num_cus, void *stream);
+
+ep_status_t ep_combine_cu(const void *y, int64_t num_rows, const int32_t *dst_row,
+                          const float *topk_weights, int32_t num_tokens, int32_t num_topk,
+                          int32_t hidden, void *out, int32_t num_cus, void *stream);
+
+/*
  * Waits for `stream`, then stores in *num_invalid the number of invalid
  * topk_idx entries (not -1 and outside [0, E)) that the most recent
  * ep_get_dispatch_layout on this workspace met.  num_invalid is a host

@@ -42,13 +42,15 @@ def ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.abs(m(a) - m(b))
 
 
-def run_gpu(case, with_combine=True, workspace=None, one_call=False):
+def run_gpu(case, with_combine=True, workspace=None, one_call=False, num_cus=0):
     """The whole path on cuda:0 (layout and dispatch as two calls, or as the
-    one ep_layout_dispatch call); returns numpy copies of every output."""
+    one ep_layout_dispatch call, optionally with a CU budget for it and for
+    combine); returns numpy copies of every output."""
     idx = torch.from_numpy(case.topk_idx).cuda()
     x = to_dev_bf16(case.x_bits)
     if one_call:
-        lay, d = ep.layout_dispatch(x, idx, case.E, case.P, workspace=workspace, fp8=case.fp8)
+        lay, d = ep.layout_dispatch(x, idx, case.E, case.P, workspace=workspace, fp8=case.fp8,
+                                    num_cus=num_cus)
     else:
         lay = ep.get_dispatch_layout(idx, case.E, case.P, workspace=workspace)
         d = ep.dispatch(x, idx, case.E, case.P, lay.workspace, fp8=case.fp8)
@@ -70,7 +72,7 @@ def run_gpu(case, with_combine=True, workspace=None, one_call=False):
     if with_combine:
         y = to_dev_bf16(case.y_bits)
         w = torch.from_numpy(case.topk_weights).cuda()
-        res["out"] = bf16_bits(ep.combine(y, d.dst_row, w))
+        res["out"] = bf16_bits(ep.combine(y, d.dst_row, w, num_cus=num_cus))
     torch.cuda.synchronize()
     return res
 
@@ -101,12 +103,13 @@ def compare(g: dict, o: dict, case, with_combine=True) -> dict:
     return stats
 
 
-def check_case(case, with_combine=True, label="", one_call=False):
-    label = (label or case.name) + (" (one call)" if one_call else "")
+def check_case(case, with_combine=True, label="", one_call=False, num_cus=0):
+    label = (label or case.name) + (" (one call)" if one_call else "") + \
+        (" (%d CUs)" % num_cus if num_cus else "")
     announce("%s T=%d H=%d E=%d P=%d K=%d fp8=%s" % (label, case.T, case.H, case.E,
                                                      case.P, case.K, case.fp8))
     t0 = time.time()
-    g = run_gpu(case, with_combine, one_call=one_call)
+    g = run_gpu(case, with_combine, one_call=one_call, num_cus=num_cus)
     t1 = time.time()
     o = run_oracle(case, with_combine)
     t2 = time.time()

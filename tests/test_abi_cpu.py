@@ -172,6 +172,19 @@ def test_dispatch_dedup_rejects_bad_arguments(buf):
     assert call(wsz=128) == WORKSPACE
 
 
+def test_cu_budget_entry_points_reject_negative_budgets(buf):
+    L = b.lib()
+    ws = buf(1 << 16)
+    p = [buf() for _ in range(12)]
+    assert L.ep_layout_dispatch_cu(p[0], 4, 256, p[1], 2, 4, 2, 0, p[2], p[3], p[4], p[5], p[6],
+                                   p[7], None, p[8], p[9], ws, 1 << 16, -1, None) == INVALID
+    assert L.ep_combine_cu(p[0], 8, p[1], p[2], 4, 2, 256, p[3], -1, None) == INVALID
+    # the other checks are those of the calls without a budget
+    assert L.ep_combine_cu(None, 8, p[1], p[2], 4, 2, 256, p[3], 4, None) == INVALID
+    assert L.ep_layout_dispatch_cu(p[0], 4, 256, p[1], 2, 6, 4, 0, p[2], p[3], p[4], p[5], p[6],
+                                   p[7], None, p[8], p[9], ws, 1 << 16, 4, None) == INVALID
+
+
 def test_low_latency_dispatch_rejects_bad_arguments(buf):
     L = b.lib()
     x, idx, cnt, rx, rs, src, dst = (buf() for _ in range(7))
