@@ -35,6 +35,8 @@
 #include "ep_internal.h"
 #include "ep_device.h"
 
+#include <atomic>
+
 namespace ep {
 namespace {
 
@@ -99,14 +101,23 @@ __device__ int block_exclusive_scan(int* a, int n, int* red) {
 // alignment is needed: the dynamic LDS need not start 8-byte aligned.)  The
 // table costs a few LDS operations per chunk instead of the ballots' VALU
 // work, which is what bounds this loop on the few workgroups a layout uses.
-template <typename Id>
+//
+// Only the first nrw waves rank; the others run side() meanwhile (work that
+// needs the staged ids but not the ranks), and everything after the first
+// barrier is shared by the whole workgroup.
+struct NoSideWork {
+    __device__ void operator()() const {}
+};
+
+template <typename Id, typename Side = NoSideWork>
 __device__ void rank_entries(const Id* ids, int n, int E, int ebits, int* wcnt, int* rnk,
-                             int* blk_cnt, unsigned* mtab = nullptr) {
+                             int* blk_cnt, unsigned* mtab = nullptr, int nrw = kLayoutWaves,
+                             Side side = Side()) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nchunks = (n + 63) >> 6;
-    const int per = (nchunks + kLayoutWaves - 1) / kLayoutWaves;
-    const int c0 = wave * per;
+    const int per = (nchunks + nrw - 1) / nrw;
+    const int c0 = wave < nrw ? wave * per : nchunks;
     const int c1 = min(c0 + per, nchunks);
     int* myw = wcnt + wave * E;
     unsigned* myt = mtab ? mtab + (size_t)wave * 2 * E : nullptr;
@@ -143,10 +154,11 @@ __device__ void rank_entries(const Id* ids, int n, int E, int ebits, int* wcnt, 
             rnk[j] = -1;
         }
     }
+    if (wave >= nrw) side();
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kLayoutThreads) {   // prefix over waves
         int run = 0;
-        for (int w = 0; w < kLayoutWaves; ++w) {
+        for (int w = 0; w < nrw; ++w) {
             const int c = wcnt[w * E + e];
             wcnt[w * E + e] = run;
             run += c;
@@ -220,6 +232,11 @@ __host__ __device__ inline int scan_per(int E) {
 // Match tables are used up to this many experts ([waves][E][2] 32-bit words).
 constexpr int kMatchTableMaxE = 256;
 
+// Waves of the count launch that rank (the rest write the partition rows
+// meanwhile), outside the de-duplicating mode.
+constexpr int kCountRankWaves = 12;
+static_assert(kCountRankWaves < kLayoutWaves, "no waves left for the partition rows");
+
 // Ints of layout_count_kernel's partition-count array pc: P, padded with
 // zeros to 64 * scan_per(P) when it is scanned (kCountDedup).
 __host__ __device__ inline int count_pc_ints(int P, int mode) {
@@ -255,8 +272,9 @@ __device__ __forceinline__ uint32_t spread4(uint32_t x) {
 // counted into pc (one LDS atomic per member partition).
 template <typename Id>
 __device__ void partition_rows(const Id* ids, int ntok, int K, int P, uint64_t pmagic,
-                               uint8_t* out_rows, bool vec, int* pc) {
-    for (int tl = threadIdx.x; tl < ntok; tl += kLayoutThreads) {
+                               uint8_t* out_rows, bool vec, int* pc,
+                               int first = -1, int stride = kLayoutThreads) {
+    for (int tl = first < 0 ? (int)threadIdx.x : first; tl < ntok; tl += stride) {
         for (int w0 = 0; w0 < P; w0 += 64) {
             uint64_t mask = 0;
             for (int k = 0; k < K; ++k) {
@@ -530,8 +548,16 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
     if (nerr) atomicAdd(&s_err, nerr);
 
     unsigned* tab = use_mtab ? mtab : nullptr;
+    // Outside the de-duplicating mode the partition rows (which need only the
+    // staged ids) are written by the last waves while the first ones rank.
+    constexpr int nrw = MODE == kCountDedup ? kLayoutWaves : kCountRankWaves;
+    const auto part_rows = [&]() {
+        if constexpr (MODE != kCountDedup)
+            partition_rows(ids, tb, K, P, pmagic, in_part + (int64_t)t0 * P, vec_rows != 0, pc,
+                           tid - nrw * 64, kLayoutThreads - nrw * 64);
+    };
     if constexpr (PRE) {
-        rank_entries(ids, n, E, ebits, wcnt, rnk, bc, tab);   // ends with a barrier
+        rank_entries(ids, n, E, ebits, wcnt, rnk, bc, tab, nrw, part_rows);   // ends with a barrier
         if (tid < 64) {
             // Wave 0 alone scans the block counts; the other waves go on
             // with the rows.
@@ -546,7 +572,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
             }
         }
     } else {
-        rank_entries(ids, n, E, ebits, wcnt, rnk, cnt + (int64_t)b * E, tab);
+        rank_entries(ids, n, E, ebits, wcnt, rnk, cnt + (int64_t)b * E, tab, nrw, part_rows);
     }
     for (int j = tid; j < n; j += kLayoutThreads) {
         const int e = ids[j];
@@ -569,8 +595,6 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
             }
         }
     } else {
-        partition_rows(ids, tb, K, P, pmagic, in_part + (int64_t)t0 * P, vec_rows != 0, pc);
-        __syncthreads();
         for (int p = tid; p < P; p += kLayoutThreads) pcnt[(int64_t)b * P + p] = pc[p];
     }
     if (tid == 0) inv[b] = s_err;
@@ -660,6 +684,30 @@ size_t layout_fused_lds_bytes(int T, int K, int E, int P) {
     return sizeof(int) * ((size_t)(4 + kLayoutWaves) * E + kLayoutEntries + P) + ids;
 }
 
+namespace {
+
+// Raising a kernel's dynamic-LDS cap is a per-device attribute of the
+// function: it is set once per (kernel, device) -- remembered in one bit per
+// device of an atomic word per kernel, so concurrent callers and several
+// devices are safe -- to the largest LDS any launch here asks for
+// (kLdsCap).  Devices past 63 set it on every call.
+constexpr int kLdsCap = (int)kFusedLdsLimit;
+constexpr int kFusedLdsSlot = 0;
+constexpr int kCountLdsSlot = 1;   // + count mode
+std::atomic<uint64_t> g_lds_raised[4];
+
+hipError_t allow_large_lds(const void* fn, int slot, int bytes) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (g_lds_raised[slot].load(std::memory_order_acquire) & bit)) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) g_lds_raised[slot].fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
+
+}  // namespace
+
 bool layout_single_launch(int T, int K, int E, int P, const WsMap& m) {
     return T > 0 && m.nb <= kFusedMaxBlocks && layout_fused_lds_bytes(T, K, E, P) <= kFusedLdsLimit;
 }
@@ -704,16 +752,12 @@ hipError_t launch_layout_count(const int64_t* idx, int T, int K, int E, int P, v
     const int vec = vector_rows(P, in_part);
     const size_t lds = count_lds_bytes(E, P, mode);
     if (lds > 64 * 1024) {
-        hipError_t e = hipErrorInvalidValue;
-        if (mode == kCountDedup)
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(layout_count_kernel<kCountDedup>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        else if (mode == kCountPre)
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(layout_count_kernel<kCountPre>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        else
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(layout_count_kernel<kCountPlain>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        const void* fn = mode == kCountDedup
+                             ? reinterpret_cast<const void*>(layout_count_kernel<kCountDedup>)
+                         : mode == kCountPre
+                             ? reinterpret_cast<const void*>(layout_count_kernel<kCountPre>)
+                             : reinterpret_cast<const void*>(layout_count_kernel<kCountPlain>);
+        hipError_t e = allow_large_lds(fn, kCountLdsSlot + mode, kLdsCap);
         if (e != hipSuccess) return e;
     }
     if (mode == kCountDedup)
@@ -750,11 +794,8 @@ hipError_t launch_layout(const int64_t* idx, int T, int K, int E, int P, void* w
     const size_t fused_lds = layout_fused_lds_bytes(T, K, E, P);
     if (layout_single_launch(T, K, E, P, m)) {
         if (fused_lds > 64 * 1024) {
-            // Raise the dynamic-LDS cap (per device, so on every call: it is a
-            // host-side attribute update).
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(layout_fused_kernel),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)kFusedLdsLimit);
+            hipError_t e = allow_large_lds(reinterpret_cast<const void*>(layout_fused_kernel),
+                                           kFusedLdsSlot, kLdsCap);
             if (e != hipSuccess) return e;
         }
         hipLaunchKernelGGL(layout_fused_kernel, dim3(m.nb), dim3(kLayoutThreads), fused_lds, s,

@@ -2,7 +2,9 @@
 
 Layout, dispatch and combine are captured once with preallocated outputs and
 replayed several times, with eager work and synchronisations between the
-replays; every replay must reproduce the eager results bit for bit.
+replays; every replay must reproduce the eager results bit for bit.  The
+two-call path, the one-call path (with and without a CU budget) and the
+de-duplicated path are each captured.
 """
 import numpy as np
 import pytest
@@ -15,10 +17,16 @@ from parity import announce
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,T", [("decode", None), ("prefill", 1024), ("coarse", 3000)])
-def test_graph_replays_match_eager(name, T):
+PATHS = [("decode", None, "two_calls"), ("prefill", 1024, "two_calls"),
+         ("coarse", 3000, "two_calls"), ("prefill", 1024, "one_call"),
+         ("skewed", 3000, "one_call"), ("prefill", 2048, "budget"), ("prefill", 1024, "dedup"),
+         ("coarse", 3000, "dedup")]
+
+
+@pytest.mark.parametrize("name,T,path", PATHS, ids=["%s-%s-%s" % p for p in PATHS])
+def test_graph_replays_match_eager(name, T, path):
     case = wl.make(name, T=T)
-    announce("graph replay %s T=%d" % (name, case.T))
+    announce("graph replay %s T=%d %s" % (name, case.T, path))
     dev = torch.device("cuda:0")
     idx = torch.from_numpy(case.topk_idx).to(dev)
     x = torch.from_numpy(case.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -34,24 +42,49 @@ def test_graph_replays_match_eager(name, T):
                         torch.empty(E + 1, dtype=torch.int32, device=dev),
                         torch.empty(P + 1, dtype=torch.int32, device=dev),
                         ep.new_workspace(T, K, E, P, dev))
-        d = ep.Dispatched(
-            torch.empty((R, H), dtype=torch.uint8 if case.fp8 else torch.bfloat16, device=dev),
-            torch.empty((R, H // 128), dtype=torch.float32, device=dev) if case.fp8 else None,
-            torch.empty(R, dtype=torch.int32, device=dev),
-            torch.empty((T, K), dtype=torch.int32, device=dev))
+        if path == "dedup":
+            RD = T * min(K, P)
+            d = ep.DedupDispatched(
+                torch.empty(P + 1, dtype=torch.int32, device=dev),
+                torch.empty((RD, H), dtype=torch.uint8 if case.fp8 else torch.bfloat16,
+                            device=dev),
+                torch.empty((RD, H // 128), dtype=torch.float32, device=dev) if case.fp8 else None,
+                torch.empty(RD, dtype=torch.int32, device=dev),
+                torch.empty((RD, K), dtype=torch.int32, device=dev),
+                torch.empty(T * K, dtype=torch.int32, device=dev),
+                torch.empty((T, K), dtype=torch.int32, device=dev))
+        else:
+            d = ep.Dispatched(
+                torch.empty((R, H), dtype=torch.uint8 if case.fp8 else torch.bfloat16, device=dev),
+                torch.empty((R, H // 128), dtype=torch.float32, device=dev) if case.fp8 else None,
+                torch.empty(R, dtype=torch.int32, device=dev),
+                torch.empty((T, K), dtype=torch.int32, device=dev))
         return lay, d, torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
+    budget = 37 if path == "budget" else 0
+
     def step(lay, d, out):
-        ep.get_dispatch_layout(idx, E, P, workspace=lay.workspace, out=lay)
-        ep.dispatch(x, idx, E, P, lay.workspace, fp8=case.fp8, out=d)
-        ep.combine(y, d.dst_row, w, out=out)
+        if path == "two_calls":
+            ep.get_dispatch_layout(idx, E, P, workspace=lay.workspace, out=lay)
+            ep.dispatch(x, idx, E, P, lay.workspace, fp8=case.fp8, out=d)
+        elif path == "dedup":
+            ep.dispatch_dedup(x, idx, E, P, workspace=lay.workspace, fp8=case.fp8, out_layout=lay,
+                              out=d)
+        else:
+            ep.layout_dispatch(x, idx, E, P, workspace=lay.workspace, fp8=case.fp8,
+                               out_layout=lay, out=d, num_cus=budget)
+        ep.combine(y, d.dst_row, w, out=out, num_cus=budget)
 
     def snapshot(lay, d, out):
-        n = int(lay.expert_offsets[-1].item())
         tensors = [lay.num_tokens_per_expert, lay.num_tokens_per_partition,
                    lay.is_token_in_partition, lay.expert_offsets, lay.partition_offsets,
-                   d.recv_src_token, d.dst_row, d.recv_x[:n].view(torch.uint8),
-                   out.view(torch.int16)]
+                   d.recv_src_token, d.dst_row, out.view(torch.int16)]
+        if path == "dedup":
+            n = int(d.partition_token_offsets[-1].item())
+            tensors += [d.partition_token_offsets, d.recv_topk_idx, d.slot_src_row]
+        else:
+            n = int(lay.expert_offsets[-1].item())
+        tensors.append(d.recv_x[:n].view(torch.uint8))
         if case.fp8:
             tensors.append(d.recv_scales[:n])
         return [t.cpu().numpy().copy() for t in tensors]
