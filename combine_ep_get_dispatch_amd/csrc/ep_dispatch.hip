@@ -140,31 +140,48 @@ __device__ __forceinline__ void store_chunk(const ChunkData& d, int H, int K, in
     }
 }
 
-// Scatter token t (one workgroup of nw waves): wave w handles chunks w, w+nw,
-// ...; `first` is chunk `wave`, already loaded (when wave < nchunk).  FP8: the
+// Scatter token t with a group of nw waves (the whole workgroup, or one of
+// several groups of a workgroup that carries several tokens at once; wave =
+// the wave's index inside its group): wave w handles chunks w, w+nw, ...;
+// `first` is chunk `wave`, already loaded (when wave < nchunk).  FP8: the
 // token's G scales are gathered in s_scale (LDS) and each destination's scale
-// row then goes out as one contiguous store.
+// row then goes out as one contiguous store.  `active` is false for a group
+// without a token, which still takes part in the barrier.
+template <bool FP8>
+__device__ __forceinline__ void scatter_token_group(const uint16_t* __restrict__ x, int H, int K,
+                                                    int t, int drow, const ChunkData& first,
+                                                    void* __restrict__ recv_x,
+                                                    float* __restrict__ recv_scales,
+                                                    float* s_scale, int nchunk, bool active,
+                                                    int wave, int nw) {
+    const int lane = threadIdx.x & 63;
+    if (active) {
+        if (wave < nchunk) store_chunk<FP8>(first, H, K, wave, drow, recv_x);
+        for (int c = wave + nw; c < nchunk; c += nw)
+            store_chunk<FP8>(load_chunk<FP8>(x, H, t, c, s_scale), H, K, c, drow, recv_x);
+    }
+    if constexpr (FP8) {
+        __syncthreads();
+        if (active) {
+            const int G = H >> 7;
+            for (int k = wave; k < K; k += nw) {   // one wave per destination scale row
+                const int r = __builtin_amdgcn_readlane(drow, k);
+                if (r < 0) continue;
+                for (int g = lane; g < G; g += 64) recv_scales[(int64_t)r * G + g] = s_scale[g];
+            }
+        }
+    }
+}
+
+// scatter_token_group for a whole workgroup.
 template <bool FP8>
 __device__ __forceinline__ void scatter_token(const uint16_t* __restrict__ x, int H, int K, int t,
                                               int drow, const ChunkData& first,
                                               void* __restrict__ recv_x,
                                               float* __restrict__ recv_scales, float* s_scale,
                                               int nchunk) {
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nw = blockDim.x >> 6;
-    if (wave < nchunk) store_chunk<FP8>(first, H, K, wave, drow, recv_x);
-    for (int c = wave + nw; c < nchunk; c += nw)
-        store_chunk<FP8>(load_chunk<FP8>(x, H, t, c, s_scale), H, K, c, drow, recv_x);
-    if constexpr (FP8) {
-        __syncthreads();
-        const int G = H >> 7;
-        for (int k = wave; k < K; k += nw) {   // one wave per destination scale row
-            const int r = __builtin_amdgcn_readlane(drow, k);
-            if (r < 0) continue;
-            for (int g = lane; g < G; g += 64) recv_scales[(int64_t)r * G + g] = s_scale[g];
-        }
-    }
+    scatter_token_group<FP8>(x, H, K, t, drow, first, recv_x, recv_scales, s_scale, nchunk, true,
+                             __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), blockDim.x >> 6);
 }
 
 template <bool FP8>
@@ -235,10 +252,10 @@ __device__ __forceinline__ void layout_dispatch_token(
     int32_t* __restrict__ off_e, int32_t* __restrict__ off_p, void* __restrict__ recv_x,
     float* __restrict__ recv_scales, int32_t* __restrict__ recv_src,
     int32_t* __restrict__ dst_row, int nchunk, int nrows, float* s_scale, int* s_row,
-    int& s_n) {
-    const int tid = threadIdx.x;
+    int& s_n, bool active, int tid, int gsize) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nw = gsize >> 6;
 
     {
         const int b = t / TB;
@@ -246,7 +263,8 @@ __device__ __forceinline__ void layout_dispatch_token(
         const int k = tid >> seg_log2;
         const int j = tid & (S - 1);
         int pk = -1, v = 0;
-        if (k < K) {
+        if (!active) {
+        } else if (k < K) {
             pk = rows[(int64_t)t * K + k];
             if (pk >= 0 && j < nb) {
                 const int e = pk >> kRankBits;
@@ -257,7 +275,7 @@ __device__ __forceinline__ void layout_dispatch_token(
             v = pre[(int64_t)j * (E + 1) + E];
         }
         for (int o = S >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-        if (j == 0) {
+        if (active && j == 0) {
             if (k < K) {
                 int r = pk >= 0 ? v + (pk & ((1 << kRankBits) - 1)) : -1;
                 if (r >= nrows) r = -1;    // only with a workspace from another layout
@@ -268,17 +286,17 @@ __device__ __forceinline__ void layout_dispatch_token(
         }
     }
     __syncthreads();
-    const int drow = lane < K ? s_row[lane] : -1;
-    if (wave == 0 && lane < K) {
+    const int drow = (active && lane < K) ? s_row[lane] : -1;
+    if (active && wave == 0 && lane < K) {
         dst_row[(int64_t)t * K + lane] = drow;
         if (drow >= 0) recv_src[drow] = t;
         const int r = t * K + lane;        // rows past the last valid one belong to no token
         if (r >= s_n) recv_src[r] = -1;
     }
-    if (t == 0 && tid == 0) hdr->num_valid = s_n;
+    if (active && t == 0 && tid == 0) hdr->num_valid = s_n;
 
-    if (t == 0) {                          // the layout's own outputs
-        for (int e = tid; e <= E; e += blockDim.x) {
+    if (active && t == 0) {                // the layout's own outputs
+        for (int e = tid; e <= E; e += gsize) {
             int c = 0, o = 0;
             for (int j = 0; j < nb; ++j) {
                 o += pre[(int64_t)j * (E + 1) + e];
@@ -288,7 +306,7 @@ __device__ __forceinline__ void layout_dispatch_token(
             if (e < E) cnt_e[e] = c;
             if (e % Ep == 0) off_p[e / Ep] = o;     // e = P*Ep = E gives off_p[P] = N
         }
-        for (int p = tid; p < P; p += blockDim.x) {
+        for (int p = tid; p < P; p += gsize) {
             int c = 0;
             for (int j = 0; j < nb; ++j) c += pcnt[(int64_t)j * P + p];
             cnt_p[p] = c;
@@ -301,8 +319,9 @@ __device__ __forceinline__ void layout_dispatch_token(
     }
 
     ChunkData first;
-    if (wave < nchunk) first = load_chunk<FP8>(x, H, t, wave, s_scale);
-    scatter_token<FP8>(x, H, K, t, drow, first, recv_x, recv_scales, s_scale, nchunk);
+    if (active && wave < nchunk) first = load_chunk<FP8>(x, H, t, wave, s_scale);
+    scatter_token_group<FP8>(x, H, K, t, drow, first, recv_x, recv_scales, s_scale, nchunk,
+                             active, wave, nw);
 }
 
 // One workgroup per token, or (LOOP, the CU-budget form) a smaller grid whose
@@ -315,22 +334,29 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void layout_dispatch_kernel(
     WsHeader* __restrict__ hdr, int32_t* __restrict__ cnt_e, int32_t* __restrict__ cnt_p,
     int32_t* __restrict__ off_e, int32_t* __restrict__ off_p, void* __restrict__ recv_x,
     float* __restrict__ recv_scales, int32_t* __restrict__ recv_src,
-    int32_t* __restrict__ dst_row, int nchunk, int nrows) {
-    extern __shared__ float s_scale[];   // [G] scales of this token (FP8)
-    __shared__ int s_row[64];            // receive row of slot k (K <= 64)
-    __shared__ int s_n;                  // N
+    int32_t* __restrict__ dst_row, int nchunk, int nrows, int gsize_loop) {
+    extern __shared__ float s_scale[];   // [groups][G] scales of the group's token (FP8)
+    __shared__ int s_row[kBudgetGroups][64];   // receive row of slot k (K <= 64)
+    __shared__ int s_n[kBudgetGroups];         // N
     if constexpr (!LOOP) {
         layout_dispatch_token<FP8>(blockIdx.x, x, H, K, E, P, Ep, TB, nb, seg_log2, cnt, pre,
                                    pcnt, inv, rows, hdr, cnt_e, cnt_p, off_e, off_p, recv_x,
-                                   recv_scales, recv_src, dst_row, nchunk, nrows, s_scale, s_row,
-                                   s_n);
+                                   recv_scales, recv_src, dst_row, nchunk, nrows, s_scale,
+                                   s_row[0], s_n[0], true, threadIdx.x, blockDim.x);
     } else {
-        for (int t = blockIdx.x; t < T; t += gridDim.x) {
-            layout_dispatch_token<FP8>(t, x, H, K, E, P, Ep, TB, nb, seg_log2, cnt, pre, pcnt,
-                                       inv, rows, hdr, cnt_e, cnt_p, off_e, off_p, recv_x,
-                                       recv_scales, recv_src, dst_row, nchunk, nrows, s_scale,
-                                       s_row, s_n);
-            __syncthreads();               // the next token reuses the LDS
+        // groups of gsize threads, one token each, in lockstep through the
+        // barriers; the workgroup's groups take tokens base + g
+        const int groups = blockDim.x / gsize_loop;
+        const int g = threadIdx.x / gsize_loop;
+        const int G = H >> 7;
+        for (int base = blockIdx.x * groups; base < T; base += gridDim.x * groups) {
+            const int t = base + g;
+            layout_dispatch_token<FP8>(t < T ? t : T - 1, x, H, K, E, P, Ep, TB, nb, seg_log2, cnt,
+                                       pre, pcnt, inv, rows, hdr, cnt_e, cnt_p, off_e, off_p,
+                                       recv_x, recv_scales, recv_src, dst_row, nchunk, nrows,
+                                       s_scale + (FP8 ? g * G : 0), s_row[g], s_n[g], t < T,
+                                       threadIdx.x - g * gsize_loop, gsize_loop);
+            __syncthreads();               // the next tokens reuse the LDS
         }
     }
 }
@@ -708,21 +734,29 @@ hipError_t launch_layout_dispatch(const uint16_t* x, const int64_t* idx, int T, 
     const int* pre = reinterpret_cast<const int*>(base + m.pre_off);
     const int* rows = reinterpret_cast<const int*>(base + m.rows_off);
     const size_t lds = fp8 ? sizeof(float) * (size_t)(H / 128) : 0;
-    const bool loop = num_cus > 0 && num_cus < T;
+    // CU budget: num_cus workgroups, each carrying `groups` tokens at a time
+    // (as many groups of nw waves as fit in one workgroup, up to
+    // kBudgetGroups), so that a CU keeps several tokens' loads in flight.
+    int groups = kDispatchMaxThreads / (64 * nw);
+    if (groups > kBudgetGroups) groups = kBudgetGroups;
+    const bool loop = num_cus > 0 && (int64_t)num_cus * groups < T;
     const dim3 grid(loop ? (unsigned)num_cus : (unsigned)T);
+    const dim3 block(loop ? 64 * nw * groups : 64 * nw);
+    const size_t lds_all = loop ? lds * groups : lds;
 #define EP_LD_ARGS x, T, H, K, E, P, E / P, m.tb, m.nb, seg_log2, cnt, pre, pcnt, inv, rows, hdr, \
-                   cnt_e, cnt_p, off_e, off_p, recv_x, recv_scales, recv_src, dst_row, nchunk, T * K
+                   cnt_e, cnt_p, off_e, off_p, recv_x, recv_scales, recv_src, dst_row, nchunk, \
+                   T * K, 64 * nw
     if (fp8 && loop)
-        hipLaunchKernelGGL((layout_dispatch_kernel<true, true>), grid, dim3(64 * nw), lds, s,
+        hipLaunchKernelGGL((layout_dispatch_kernel<true, true>), grid, block, lds_all, s,
                            EP_LD_ARGS);
     else if (fp8)
-        hipLaunchKernelGGL((layout_dispatch_kernel<true, false>), grid, dim3(64 * nw), lds, s,
+        hipLaunchKernelGGL((layout_dispatch_kernel<true, false>), grid, block, lds_all, s,
                            EP_LD_ARGS);
     else if (loop)
-        hipLaunchKernelGGL((layout_dispatch_kernel<false, true>), grid, dim3(64 * nw), lds, s,
+        hipLaunchKernelGGL((layout_dispatch_kernel<false, true>), grid, block, lds_all, s,
                            EP_LD_ARGS);
     else
-        hipLaunchKernelGGL((layout_dispatch_kernel<false, false>), grid, dim3(64 * nw), lds, s,
+        hipLaunchKernelGGL((layout_dispatch_kernel<false, false>), grid, block, lds_all, s,
                            EP_LD_ARGS);
 #undef EP_LD_ARGS
     return hipGetLastError();

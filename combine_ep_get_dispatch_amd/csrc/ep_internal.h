@@ -12,6 +12,8 @@ namespace ep {
 // size (or the kernel's own size) that loop over their work, so that the
 // hardware places them on at most num_cus CUs.
 constexpr int kBudgetThreads = 1024;
+// Tokens a CU-budget dispatch workgroup carries at once (at most).
+constexpr int kBudgetGroups = 4;
 
 // ---------------------------------------------------------------- layout ---
 // The layout kernel gives each workgroup one block of consecutive tokens
