@@ -32,6 +32,7 @@
 //   (expert << 12 | rank in block); finalize sums the count matrix per
 //   workgroup (E * nb ints), scans the totals and rewrites the slots as
 //   receive rows  row = expert_offsets[e] + (rows of e in blocks < b) + rank.
+#include "ep.h"
 #include "ep_internal.h"
 #include "ep_device.h"
 
@@ -104,15 +105,17 @@ __device__ int block_exclusive_scan(int* a, int n, int* red) {
 //
 // Only the first nrw waves rank; the others run side() meanwhile (work that
 // needs the staged ids but not the ranks), and everything after the first
-// barrier is shared by the whole workgroup.
+// barrier is shared by the whole workgroup.  mid() runs on every thread
+// between the first and the second barrier (it sees what side() wrote, and
+// what it writes is seen by everything after the call).
 struct NoSideWork {
     __device__ void operator()() const {}
 };
 
-template <typename Id, typename Side = NoSideWork>
+template <typename Id, typename Side = NoSideWork, typename Mid = NoSideWork>
 __device__ void rank_entries(const Id* ids, int n, int E, int ebits, int* wcnt, int* rnk,
                              int* blk_cnt, unsigned* mtab = nullptr, int nrw = kLayoutWaves,
-                             Side side = Side()) {
+                             Side side = Side(), Mid mid = Mid()) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nchunks = (n + 63) >> 6;
@@ -165,6 +168,7 @@ __device__ void rank_entries(const Id* ids, int n, int E, int ebits, int* wcnt, 
         }
         if (blk_cnt) blk_cnt[e] = run;
     }
+    mid();
     __syncthreads();
     for (int j = threadIdx.x; j < n; j += kLayoutThreads) {
         const int e = ids[j];
@@ -223,7 +227,7 @@ __device__ void scan_block_counts(const int* bc, int E, int* cnt, int* pre) {
 
 // Per-lane share of experts for scan_block_counts: ceil(E / 64) rounded up to
 // a power of two (<= 16 for E <= 1024).
-__host__ __device__ inline int scan_per(int E) {
+__host__ __device__ constexpr int scan_per(int E) {
     int per = 1;
     while (per * 64 < E) per <<= 1;
     return per;
@@ -232,25 +236,33 @@ __host__ __device__ inline int scan_per(int E) {
 // Match tables are used up to this many experts ([waves][E][2] 32-bit words).
 constexpr int kMatchTableMaxE = 256;
 
-// Waves of the count launch that rank (the rest write the partition rows
-// meanwhile), outside the de-duplicating mode.
+// Waves of the count launch that rank; the other kCountSideWaves write the
+// partition rows meanwhile (and, in the de-duplicating mode, rank the tokens
+// inside their partitions).
 constexpr int kCountRankWaves = 12;
-static_assert(kCountRankWaves < kLayoutWaves, "no waves left for the partition rows");
+constexpr int kCountSideWaves = kLayoutWaves - kCountRankWaves;
+static_assert(kCountSideWaves > 0, "no waves left for the partition rows");
+
+// Flag on a side wave's partition rank: the token is the highest member of
+// its pass in the slot's partition (ranks stay below kLayoutEntries).
+constexpr int kSideTop = 1 << 30;
 
 // Ints of layout_count_kernel's partition-count array pc: P, padded with
 // zeros to 64 * scan_per(P) when it is scanned (kCountDedup).
-__host__ __device__ inline int count_pc_ints(int P, int mode) {
+__host__ __device__ constexpr int count_pc_ints(int P, int mode) {
     return mode == kCountDedup ? 64 * scan_per(P) : P;
 }
 
 // layout_count_kernel's dynamic LDS, in ints: wcnt [waves][E], ids and rnk
 // [kLayoutEntries] each, pc [count_pc_ints], with kCountPre or kCountDedup bc
-// [64 * scan_per(E)], with kCountDedup the partition ballots wb [waves][128];
-// the match tables follow at the returned offset.
-__host__ __device__ inline int count_table_offset(int E, int P, int mode) {
+// [64 * scan_per(E)], with kCountDedup the side waves' partition match tables
+// ptab [kCountSideWaves][P][2], their member counts prun [kCountSideWaves][P]
+// and the slots' partition ranks psr [kLayoutEntries]; the expert match
+// tables follow at the returned offset.
+__host__ __device__ constexpr int count_table_offset(int E, int P, int mode) {
     return kLayoutWaves * E + 2 * kLayoutEntries + count_pc_ints(P, mode) +
            (mode != kCountPlain ? 64 * scan_per(E) : 0) +
-           (mode == kCountDedup ? kLayoutWaves * 128 : 0);
+           (mode == kCountDedup ? 3 * kCountSideWaves * P + kLayoutEntries : 0);
 }
 
 // Partition of expert e: e / Ep computed as (e * ceil(2^32 / Ep)) >> 32,
@@ -263,6 +275,22 @@ __device__ __forceinline__ int partition_of(int e, uint64_t pmagic) {
 // Four membership bits (bit i of x, i < 4) as four bytes 0/1.
 __device__ __forceinline__ uint32_t spread4(uint32_t x) {
     return (x & 1u) | ((x & 2u) << 7) | ((x & 4u) << 14) | ((x & 8u) << 21);
+}
+
+// One token's membership bytes for 64 partitions or fewer (nbytes), from
+// their bit mask; 16-byte stores when vec (nbytes a multiple of 16, row
+// 16-byte aligned).
+__device__ __forceinline__ void write_member_row(uint8_t* row, uint64_t mask, int nbytes,
+                                                 bool vec) {
+    if (vec) {
+        for (int q = 0; q < nbytes; q += 16) {
+            const uint32_t b16 = (uint32_t)(mask >> q) & 0xffffu;
+            *reinterpret_cast<uint4*>(row + q) =
+                make_uint4(spread4(b16), spread4(b16 >> 4), spread4(b16 >> 8), spread4(b16 >> 12));
+        }
+    } else {
+        for (int q = 0; q < nbytes; ++q) row[q] = (uint8_t)((mask >> q) & 1u);
+    }
 }
 
 // Partition-membership rows of tokens [0, ntok) (thread per token; ids are
@@ -286,113 +314,140 @@ __device__ void partition_rows(const Id* ids, int ntok, int K, int P, uint64_t p
             if (pc) {
                 for (uint64_t m = mask; m; m &= m - 1) atomicAdd(&pc[w0 + __builtin_ctzll(m)], 1);
             }
-            if (out_rows) {
-                const int nbytes = min(64, P - w0);
-                uint8_t* row = out_rows + (int64_t)tl * P + w0;
-                if (vec) {
-                    for (int q = 0; q < nbytes; q += 16) {
-                        const uint32_t b16 = (uint32_t)(mask >> q) & 0xffffu;
-                        *reinterpret_cast<uint4*>(row + q) =
-                            make_uint4(spread4(b16), spread4(b16 >> 4), spread4(b16 >> 8),
-                                       spread4(b16 >> 12));
-                    }
-                } else {
-                    for (int q = 0; q < nbytes; ++q) row[q] = (uint8_t)((mask >> q) & 1u);
-                }
-            }
+            if (out_rows)
+                write_member_row(out_rows + (int64_t)tl * P + w0, mask, min(64, P - w0), vec);
         }
     }
 }
 
-// Partition-membership rows of tokens [0, ntok) as partition_rows writes
-// them, plus each slot's rank among the block's member tokens of its slot's
-// partition (token order), for the de-duplicated dispatch.  Tokens go in
-// passes of one per thread; within a pass a wave's lanes are consecutive
-// tokens, so for every partition q of a 64-partition window one ballot of
-// "member of q" gives the members' ranks inside the wave.  Lane q keeps
-// partition q's ballot and stores it in the wave's LDS row wb; each slot then
-// reads the ballot of its own partition once and takes the popcount of the
-// lanes below.  An exclusive prefix over the waves (plus the earlier passes,
-// kept in pc) makes the ranks ranks inside the block.  wp is [waves][P] LDS
-// scratch, wb [waves][64][2] LDS scratch, srank [ntok*K] LDS scratch, pc [P]
-// zeroed LDS that ends holding the block's member-token count per partition;
-// prank [ntok*K] (global) receives the ranks (-1 for slots without an
-// expert).
+// Tokens per side wave in the de-duplicating count launch: the block's ntok
+// tokens in ns contiguous spans, whole passes of 64.
+__host__ __device__ inline int side_span(int ntok, int ns) {
+    return ((ntok + ns - 1) / ns + 63) & ~63;
+}
+
+// Slots a side wave handles at once (their partitions and ranks in registers).
+constexpr int kSideChunk = 8;
+
+// Side wave s (of ns) of the de-duplicating count launch: the partition rows
+// of tokens [s*span, (s+1)*span) (as partition_rows writes them) and, for
+// each of their slots, the token's rank among the span's member tokens of
+// the slot's partition (token order).  Tokens go in passes of 64, lane =
+// token.  Within a pass the members of partition p come from the wave's LDS
+// match table tab[p] (two 32-bit words: lanes 0-31 and 32-63): every slot
+// ORs its lane's bit into its partition's entry, reads the entry back and
+// takes run[p] (the span's members of p in the earlier passes) plus the
+// members below its lane; then every slot clears its entry, and the highest
+// member stores run[p] = its rank + 1.  A token with several slots in p sets
+// the same bit and stores the same values, so no slot needs to know whether
+// it is its token's first in p.  One wave's LDS operations complete in issue
+// order, so each read sees all of the pass's bits and the clears and stores
+// follow every read.  Slots go kSideChunk at a time so that their LDS loads
+// are issued together; with K <= kSideChunk a token's partitions and ranks
+// stay in registers through the pass (and, with P <= 64, give its membership
+// row too).  srank[slot] gets the rank (with kSideTop on the highest member's
+// slots); run[s][p] ends holding the span's member count of p.  tab and run
+// start zeroed; tab ends zeroed.
 template <typename Id>
-__device__ void partition_ranks(const Id* ids, int ntok, int K, int P, uint64_t pmagic,
-                                uint8_t* out_rows, bool vec, int* wp, unsigned* wb, int* srank,
-                                int* pc, int* prank) {
+__device__ void partition_ranks_side(const Id* ids, int ntok, int K, int P, uint64_t pmagic,
+                                     uint8_t* out_rows, bool vec, unsigned* tab, int* run,
+                                     int* srank, int s, int ns) {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
     const uint64_t below = (1ull << lane) - 1ull;
-    for (int base = 0; base < ntok; base += kLayoutThreads) {
-        for (int i = threadIdx.x; i < kLayoutWaves * P; i += kLayoutThreads) wp[i] = 0;
-        __syncthreads();
-        const int tl = base + threadIdx.x;
-        const bool act = tl < ntok;
-        for (int w0 = 0; w0 < P; w0 += 64) {
-            uint64_t mask = 0;
-            if (act) {
-                for (int k = 0; k < K; ++k) {
-                    const int e = ids[tl * K + k];
-                    if (e < 0) continue;
-                    const int q = partition_of(e, pmagic) - w0;
-                    if (q >= 0 && q < 64) mask |= 1ull << q;
-                }
-                const int nbytes = min(64, P - w0);
-                uint8_t* row = out_rows + (int64_t)tl * P + w0;
-                if (vec) {
-                    for (int q = 0; q < nbytes; q += 16) {
-                        const uint32_t b16 = (uint32_t)(mask >> q) & 0xffffu;
-                        *reinterpret_cast<uint4*>(row + q) =
-                            make_uint4(spread4(b16), spread4(b16 >> 4), spread4(b16 >> 8),
-                                       spread4(b16 >> 12));
-                    }
-                } else {
-                    for (int q = 0; q < nbytes; ++q) row[q] = (uint8_t)((mask >> q) & 1u);
-                }
+    const int span = side_span(ntok, ns);
+    const int t_end = min(ntok, (s + 1) * span);
+    unsigned* mytab = tab + (size_t)s * 2 * P;
+    int* myrun = run + (size_t)s * P;
+    const bool one = K <= kSideChunk;
+    if (!(one && P <= 64))
+        partition_rows(ids, t_end, K, P, pmagic, out_rows, vec, nullptr, s * span + lane, 64);
+    for (int base = s * span; base < t_end; base += 64) {
+        const int tl = base + lane;
+        if (tl >= t_end) continue;
+        const Id* tok_ids = ids + tl * K;
+        int* tok_rank = srank + tl * K;
+        int pp[kSideChunk];                // partitions of slots k0 .. k0 + 7 (-1: none)
+        int rr[kSideChunk];                // their ranks (| kSideTop)
+        const auto parts = [&](int k0) {
+#pragma unroll
+            for (int i = 0; i < kSideChunk; ++i) {
+                const int e = k0 + i < K ? (int)tok_ids[k0 + i] : -1;
+                pp[i] = e >= 0 ? partition_of(e, pmagic) : -1;
             }
-            const int nq = min(64, P - w0);
-            uint64_t mine = 0;                   // lane q: ballot of partition w0 + q
-            for (int q = 0; q < nq; ++q) {       // wave-uniform loop: ballots are safe
-                const uint64_t bb = __ballot((mask >> q) & 1ull);
-                if (lane == q) mine = bb;
+        };
+        const auto set_bits = [&]() {
+#pragma unroll
+            for (int i = 0; i < kSideChunk; ++i)
+                if (pp[i] >= 0)
+                    __hip_atomic_fetch_or(mytab + 2 * pp[i] + (lane >> 5), 1u << (lane & 31),
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+        };
+        const auto read_ranks = [&](int k0) {
+#pragma unroll
+            for (int i = 0; i < kSideChunk; ++i) {
+                if (pp[i] < 0) continue;
+                const unsigned lo = __hip_atomic_load(mytab + 2 * pp[i], __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_WAVEFRONT);
+                const unsigned hi = __hip_atomic_load(mytab + 2 * pp[i] + 1, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_WAVEFRONT);
+                const uint64_t m = ((uint64_t)hi << 32) | lo;
+                const int r = __hip_atomic_load(myrun + pp[i], __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_WAVEFRONT) +
+                              __popcll(m & below);
+                rr[i] = (m >> lane) == 1ull ? r | kSideTop : r;
+                __hip_atomic_store(tok_rank + k0 + i, rr[i], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WAVEFRONT);
             }
-            unsigned* myb = wb + wave * 128;
-            myb[2 * lane] = (unsigned)mine;
-            myb[2 * lane + 1] = (unsigned)(mine >> 32);
-            if (lane < nq) wp[wave * P + w0 + lane] = __popcll(mine);
-            // (this wave's LDS writes above complete before its reads below)
-            if (act) {
-                for (int k = 0; k < K; ++k) {
-                    const int e = ids[tl * K + k];
-                    if (e < 0) continue;
-                    const int q = partition_of(e, pmagic) - w0;
-                    if (q < 0 || q >= 64) continue;
-                    const uint64_t bq = (uint64_t)myb[2 * q] | ((uint64_t)myb[2 * q + 1] << 32);
-                    srank[tl * K + k] = __popcll(bq & below);
-                }
+        };
+        const auto clear = [&]() {
+#pragma unroll
+            for (int i = 0; i < kSideChunk; ++i) {
+                if (pp[i] < 0) continue;
+                __hip_atomic_store(mytab + 2 * pp[i], 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WAVEFRONT);
+                __hip_atomic_store(mytab + 2 * pp[i] + 1, 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WAVEFRONT);
+                if (rr[i] & kSideTop)
+                    __hip_atomic_store(myrun + pp[i], (rr[i] & ~kSideTop) + 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WAVEFRONT);
+            }
+        };
+        if (one) {
+            parts(0);
+            if (P <= 64) {
+                uint64_t mask = 0;
+#pragma unroll
+                for (int i = 0; i < kSideChunk; ++i)
+                    if (pp[i] >= 0) mask |= 1ull << pp[i];
+                write_member_row(out_rows + (int64_t)tl * P, mask, P, vec);
+            }
+            set_bits();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);   // keep the phases in issue order
+            read_ranks(0);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            clear();
+        } else {
+            for (int k0 = 0; k0 < K; k0 += kSideChunk) {
+                parts(k0);
+                set_bits();
+            }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            for (int k0 = 0; k0 < K; k0 += kSideChunk) {
+                parts(k0);
+                read_ranks(k0);
+            }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            for (int k0 = 0; k0 < K; k0 += kSideChunk) {
+                parts(k0);
+#pragma unroll
+                for (int i = 0; i < kSideChunk; ++i)
+                    if (pp[i] >= 0)
+                        rr[i] = __hip_atomic_load(tok_rank + k0 + i, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_WAVEFRONT);
+                clear();
             }
         }
-        __syncthreads();
-        for (int p = threadIdx.x; p < P; p += kLayoutThreads) {   // prefix over waves
-            int run = pc[p];
-            for (int w = 0; w < kLayoutWaves; ++w) {
-                const int c = wp[w * P + p];
-                wp[w * P + p] = run;
-                run += c;
-            }
-            pc[p] = run;
-        }
-        __syncthreads();
-        if (act) {
-            for (int k = 0; k < K; ++k) {
-                const int e = ids[tl * K + k];
-                prank[tl * K + k] =
-                    e >= 0 ? wp[wave * P + partition_of(e, pmagic)] + srank[tl * K + k] : -1;
-            }
-        }
-        __syncthreads();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
 }
 
@@ -507,6 +562,10 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
     int* rnk = ids + kLayoutEntries;               // [kLayoutEntries]
     int* pc = rnk + kLayoutEntries;                // [count_pc_ints(P, MODE)]
     int* bc = pc + count_pc_ints(P, MODE);         // [64 * scan_per(E)] block counts (PRE)
+    // kCountDedup: the side waves' partition tables, member counts and ranks
+    unsigned* ptab = reinterpret_cast<unsigned*>(bc + (PRE ? 64 * scan_per(E) : 0));
+    int* prun = reinterpret_cast<int*>(ptab + 2 * kCountSideWaves * P);   // [side waves][P]
+    int* psr = prun + kCountSideWaves * P;                                // [kLayoutEntries]
     // [waves][E][2] match tables (E <= kMatchTableMaxE)
     unsigned* mtab = reinterpret_cast<unsigned*>(smem + count_table_offset(E, P, MODE));
     const bool use_mtab = E <= kMatchTableMaxE;
@@ -533,6 +592,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
         for (int i = E + tid; i < 64 * scan_per(E); i += kLayoutThreads) bc[i] = 0;
     if (use_mtab)
         for (int i = tid; i < 2 * kLayoutWaves * E; i += kLayoutThreads) mtab[i] = 0u;
+    if (MODE == kCountDedup)                       // ptab and prun
+        for (int i = tid; i < 3 * kCountSideWaves * P; i += kLayoutThreads) ptab[i] = 0u;
     if (tid == 0) s_err = 0;
     int nerr = 0;
 #pragma unroll
@@ -548,19 +609,40 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
     if (nerr) atomicAdd(&s_err, nerr);
 
     unsigned* tab = use_mtab ? mtab : nullptr;
-    // Outside the de-duplicating mode the partition rows (which need only the
-    // staged ids) are written by the last waves while the first ones rank.
-    constexpr int nrw = MODE == kCountDedup ? kLayoutWaves : kCountRankWaves;
-    const auto part_rows = [&]() {
-        if constexpr (MODE != kCountDedup)
+    // The last kCountSideWaves waves write the partition rows (which need
+    // only the staged ids) while the first ones rank; in the de-duplicating
+    // mode they also rank the tokens inside their partitions, and between
+    // the ranking's barriers every thread turns their per-span member counts
+    // into prefixes over the spans (pc = the block's totals).
+    constexpr int nrw = kCountRankWaves;
+    [[maybe_unused]] const int side_tok = side_span(tb, kCountSideWaves);
+    const auto side = [&]() {
+        if constexpr (MODE == kCountDedup)
+            partition_ranks_side(ids, tb, K, P, pmagic, in_part + (int64_t)t0 * P,
+                                 vec_rows != 0, ptab, prun, psr,
+                                 __builtin_amdgcn_readfirstlane(tid >> 6) - nrw, kCountSideWaves);
+        else
             partition_rows(ids, tb, K, P, pmagic, in_part + (int64_t)t0 * P, vec_rows != 0, pc,
                            tid - nrw * 64, kLayoutThreads - nrw * 64);
     };
+    const auto mid = [&]() {
+        if constexpr (MODE == kCountDedup) {
+            for (int p = tid; p < P; p += kLayoutThreads) {
+                int run = 0;
+                for (int w = 0; w < kCountSideWaves; ++w) {
+                    const int c = prun[w * P + p];
+                    prun[w * P + p] = run;
+                    run += c;
+                }
+                pc[p] = run;
+            }
+        }
+    };
     if constexpr (PRE) {
-        rank_entries(ids, n, E, ebits, wcnt, rnk, bc, tab, nrw, part_rows);   // ends with a barrier
+        rank_entries(ids, n, E, ebits, wcnt, rnk, bc, tab, nrw, side, mid);   // ends with a barrier
+        // One wave scans the block's expert counts and (de-duplicating mode)
+        // another its partition counts; the other waves go on with the rows.
         if (tid < 64) {
-            // Wave 0 alone scans the block counts; the other waves go on
-            // with the rows.
             int* cb = cnt + (int64_t)b * E;
             int* pb = pre + (int64_t)b * (E + 1);
             switch (scan_per(E)) {
@@ -570,20 +652,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
                 case 8: scan_block_counts<8>(bc, E, cb, pb); break;
                 default: scan_block_counts<16>(bc, E, cb, pb); break;
             }
-        }
-    } else {
-        rank_entries(ids, n, E, ebits, wcnt, rnk, cnt + (int64_t)b * E, tab, nrw, part_rows);
-    }
-    for (int j = tid; j < n; j += kLayoutThreads) {
-        const int e = ids[j];
-        rows[(int64_t)t0 * K + j] = (e >= 0) ? (e << kRankBits) | rnk[j] : -1;
-    }
-    if constexpr (MODE == kCountDedup) {
-        __syncthreads();                           // rnk and wcnt are free from here
-        partition_ranks(ids, tb, K, P, pmagic, in_part + (int64_t)t0 * P, vec_rows != 0, wcnt,
-                        reinterpret_cast<unsigned*>(bc + 64 * scan_per(E)), rnk, pc,
-                        prank + (int64_t)t0 * K);    // ends with a barrier
-        if (tid < 64) {
+        } else if (MODE == kCountDedup && tid < 128) {
             int* cb = pcnt + (int64_t)b * P;
             int* pb = ppre + (int64_t)b * (P + 1);
             switch (scan_per(P)) {
@@ -595,8 +664,19 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
             }
         }
     } else {
-        for (int p = tid; p < P; p += kLayoutThreads) pcnt[(int64_t)b * P + p] = pc[p];
+        rank_entries(ids, n, E, ebits, wcnt, rnk, cnt + (int64_t)b * E, tab, nrw, side);
     }
+    for (int j = tid; j < n; j += kLayoutThreads) {
+        const int e = ids[j];
+        rows[(int64_t)t0 * K + j] = (e >= 0) ? (e << kRankBits) | rnk[j] : -1;
+        if constexpr (MODE == kCountDedup) {
+            const int w = (j / K) / side_tok;      // the side wave that ranked the token
+            prank[(int64_t)t0 * K + j] =
+                e >= 0 ? prun[w * P + partition_of(e, pmagic)] + (psr[j] & ~kSideTop) : -1;
+        }
+    }
+    if constexpr (MODE != kCountDedup)
+        for (int p = tid; p < P; p += kLayoutThreads) pcnt[(int64_t)b * P + p] = pc[p];
     if (tid == 0) inv[b] = s_err;
 }
 
@@ -730,7 +810,12 @@ bool vector_rows(int P, const uint8_t* in_part) {
 
 }  // namespace
 
-// Dynamic LDS of layout_count_kernel.
+// Dynamic LDS of layout_count_kernel; the largest shapes of each kind fit.
+static_assert(sizeof(int) * count_table_offset(EP_MAX_EXPERTS, EP_MAX_EXPERTS, kCountDedup) <=
+                  (size_t)kLdsCap, "count launch LDS");
+static_assert(sizeof(int) * (count_table_offset(kMatchTableMaxE, kMatchTableMaxE, kCountDedup) +
+                             2 * kLayoutWaves * kMatchTableMaxE) <= (size_t)kLdsCap,
+              "count launch LDS with match tables");
 size_t count_lds_bytes(int E, int P, int mode) {
     size_t bytes = sizeof(int) * (size_t)count_table_offset(E, P, mode);
     if (E <= kMatchTableMaxE) bytes += sizeof(unsigned) * 2 * (size_t)kLayoutWaves * E;
