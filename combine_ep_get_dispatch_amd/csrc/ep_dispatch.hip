@@ -455,35 +455,6 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void dedup_dispatch_kernel(
     }
     const int store_row = first ? drow : -1;
 
-    if (wave == 0) {
-        if (lane < K) {
-            dst_row[(int64_t)t * K + lane] = erow;
-            if (erow >= 0) slot_src[erow] = drow;
-            const int r = t * K + lane;    // expert rows past N belong to no slot
-            if (r >= N) slot_src[r] = -1;
-            if (store_row >= 0) recv_src[store_row] = t;
-        }
-        // Local expert ids of each of this token's rows: owner slot k's row,
-        // lane j's slot.  (Spreading this and the marking below over all
-        // waves measured slower.)
-        for (int k = 0; k < K; ++k) {
-            const int rk = __builtin_amdgcn_readlane(store_row, k);
-            if (rk < 0) continue;
-            const int pk_part = __builtin_amdgcn_readlane(part, k);
-            if (lane < K)
-                recv_topk_idx[(int64_t)rk * K + lane] = (part == pk_part) ? e - pk_part * Ep : -1;
-        }
-    }
-    // Rows past the last de-duplicated one among [t*Kp, (t+1)*Kp) are unused.
-    for (int i = tid; i < Kp * (K + 1); i += blockDim.x) {
-        const int q = i / (K + 1);
-        const int c = i - q * (K + 1);
-        const int64_t r = (int64_t)t * Kp + q;
-        if (r < ND) continue;
-        if (c == K) recv_src[r] = -1;
-        else recv_topk_idx[r * K + c] = -1;
-    }
-
     if (t == 0) {                          // the layout's own outputs
         for (int ee = tid; ee <= E; ee += blockDim.x) {
             int c = 0, o = 0;
@@ -515,6 +486,43 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void dedup_dispatch_kernel(
     ChunkData first_chunk;
     if (wave < nchunk) first_chunk = load_chunk<FP8>(x, H, t, wave, s_scale);
     scatter_token<FP8>(x, H, K, t, store_row, first_chunk, recv_x, recv_scales, s_scale, nchunk);
+
+    // The token's index outputs go after its data: issued first, they delay
+    // wave 0's loads (the launch took 56.4 instead of 52.8 us at 4096 x 7168,
+    // top-8 of 256 experts).
+    if (wave == 0) {
+        if (lane < K) {
+            dst_row[(int64_t)t * K + lane] = erow;
+            if (erow >= 0) slot_src[erow] = drow;
+            const int r = t * K + lane;    // expert rows past N belong to no slot
+            if (r >= N) slot_src[r] = -1;
+            if (store_row >= 0) recv_src[store_row] = t;
+        }
+        // Local expert ids of the token's rows, one (row owner k, column c)
+        // pair per lane: the row of slot k (if it owns one) holds at column c
+        // slot c's expert minus the partition's first expert when slot c is
+        // in slot k's partition, else -1.
+        for (int l0 = 0; l0 < K * K; l0 += 64) {
+            const int l = l0 + lane;
+            const int k = l < K * K ? l / K : 0;
+            const int c = l - k * K;
+            const int rk = __shfl(store_row, k);
+            const int k_part = __shfl(part, k);
+            const int c_part = __shfl(part, c < K ? c : 0);
+            const int ec = __shfl(e, c < K ? c : 0);
+            if (l < K * K && rk >= 0)
+                recv_topk_idx[(int64_t)rk * K + c] = (c_part == k_part) ? ec - k_part * Ep : -1;
+        }
+    }
+    // Rows past the last de-duplicated one among [t*Kp, (t+1)*Kp) are unused.
+    for (int i = tid; i < Kp * (K + 1); i += blockDim.x) {
+        const int q = i / (K + 1);
+        const int c = i - q * (K + 1);
+        const int64_t r = (int64_t)t * Kp + q;
+        if (r < ND) continue;
+        if (c == K) recv_src[r] = -1;
+        else recv_topk_idx[r * K + c] = -1;
+    }
 }
 
 // T = 0 for the de-duplicated dispatch: every partition token offset is 0.
