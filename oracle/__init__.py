@@ -70,6 +70,9 @@ def _bind(lib):
     lib.oracle_dedup_layout.argtypes = [_i64p, _i32, _i32, _i32, _i32, _i32p, _i32p, _i32p,
                                         _i32p, _i32p, _i32p, _i32p]
     lib.oracle_dedup_layout.restype = _i32
+    lib.oracle_aligned_layout.argtypes = [_i64p, _i32, _i32, _i32, _i32, _i32, _i32p, _i32p,
+                                          _u8p, _i32p, _i32p, _i32p, _i32p]
+    lib.oracle_aligned_layout.restype = _i64
     return lib
 
 
@@ -290,6 +293,46 @@ def dedup_layout(topk_idx: np.ndarray, E: int, P: int) -> dict:
     res.update(dst_row=dst, recv_src_token=src, partition_token_offsets=ptok_off,
                dedup_row=dd_row, dedup_src_token=dd_src, dedup_topk_idx=dd_idx,
                slot_src_row=slot_src, num_dedup_rows=int(n))
+    return res
+
+
+def aligned_rows(T: int, K: int, E: int, align: int) -> int:
+    """Receive rows an aligned layout may use: T*K + E*(align-1)."""
+    return T * K + E * (align - 1)
+
+
+def aligned_layout(topk_idx: np.ndarray, E: int, P: int, align: int) -> dict:
+    """Expert-major layout with every expert's run padded to a multiple of
+    ``align`` rows (see ``oracle_aligned_layout``)."""
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
+    T, K = idx.shape
+    cnt_e = np.empty(E, np.int32)
+    cnt_p = np.empty(P, np.int32)
+    in_part = np.empty((T, P), np.uint8)
+    off_e = np.empty(E + 1, np.int32)
+    off_p = np.empty(P + 1, np.int32)
+    dst = np.empty((T, K), np.int32)
+    src = np.empty(aligned_rows(T, K, E, align), np.int32)
+    nerr = _load().oracle_aligned_layout(
+        _ptr(idx, ctypes.c_int64), T, K, E, P, align, _ptr(cnt_e, ctypes.c_int32),
+        _ptr(cnt_p, ctypes.c_int32), _ptr(in_part, ctypes.c_uint8), _ptr(off_e, ctypes.c_int32),
+        _ptr(off_p, ctypes.c_int32), _ptr(dst, ctypes.c_int32), _ptr(src, ctypes.c_int32))
+    return dict(num_tokens_per_expert=cnt_e, num_tokens_per_partition=cnt_p,
+                is_token_in_partition=in_part, expert_offsets=off_e, partition_offsets=off_p,
+                dst_row=dst, recv_src_token=src, num_invalid=int(nerr))
+
+
+def run_aligned(topk_idx, x_bits, E, P, align, fp8, y_bits=None, topk_weights=None) -> dict:
+    """The aligned path: layout, dispatch into the padded rows and
+    (optionally) combine of expert outputs laid out like the receive rows."""
+    res = aligned_layout(topk_idx, E, P, align)
+    src = res["recv_src_token"]
+    if fp8:
+        res["recv_x"], res["recv_scales"] = dispatch_rows_fp8(x_bits, src)
+    else:
+        res["recv_x"] = dispatch_rows_bf16(x_bits, src)
+    if y_bits is not None:
+        res["out"] = combine(y_bits, res["dst_row"], topk_weights)
     return res
 
 

@@ -399,6 +399,60 @@ void oracle_dispatch_rows_fp8(const uint16_t *x, int32_t T, int32_t H,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Expert runs aligned for grouped GEMMs                                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The expert-major layout of oracle_layout / oracle_permutation with every
+ * expert's run padded to a whole number of `align` rows, so that each
+ * expert's first row sits on a tile boundary of a grouped expert GEMM.  The
+ * pages name no such layout (the decode path's fixed-size per-expert buffers
+ * are the nearest: "DeepSeek releases DeepEP ...", section "DeepEP:
+ * Optimizing MoE Communication"); this is the plainest reading:
+ *   cnt_e, cnt_p, in_part   as oracle_layout (unpadded counts)
+ *   off_e [E+1]  off_e[0] = 0, off_e[e+1] = off_e[e] + ceil(cnt_e[e] / align) * align
+ *   off_p [P+1]  off_p[p] = off_e[p * (E/P)]
+ *   dst   [T][K] off_e[e] + (rank of slot (t,k) among expert e's valid slots
+ *                in (token, slot) order), -1 for a masked/invalid slot
+ *   src   [R]    R = T*K + E*(align-1) rows (enough for any routing): the
+ *                source token of each row, -1 for padding and unused rows
+ * align = 1 gives exactly oracle_layout and oracle_permutation.
+ * Returns the number of invalid slots (outside [0, E) and not -1).
+ */
+int64_t oracle_aligned_layout(const int64_t *idx, int32_t T, int32_t K, int32_t E, int32_t P,
+                              int32_t align, int32_t *cnt_e, int32_t *cnt_p, uint8_t *in_part,
+                              int32_t *off_e, int32_t *off_p, int32_t *dst, int32_t *src)
+{
+    int32_t Ep = E / P;
+    int64_t R = (int64_t)T * K + (int64_t)E * (align - 1);
+    int64_t nerr = oracle_layout(idx, T, K, E, P, cnt_e, cnt_p, in_part, off_e, off_p);
+    int32_t *next = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    int32_t run = 0;
+
+    for (int32_t e = 0; e < E; ++e) {
+        off_e[e] = run;
+        run += (cnt_e[e] + align - 1) / align * align;   /* the run padded to whole tiles */
+    }
+    off_e[E] = run;
+    for (int32_t p = 0; p <= P; ++p)
+        off_p[p] = off_e[Ep * p];
+
+    for (int64_t r = 0; r < R; ++r)
+        src[r] = -1;
+    for (int64_t i = 0; i < (int64_t)T * K; ++i) {      /* row-major = (token, slot) order */
+        int64_t v = idx[i];
+        dst[i] = -1;
+        if (v < 0 || v >= E)
+            continue;
+        dst[i] = off_e[v] + next[v];
+        next[v] += 1;
+        src[dst[i]] = (int32_t)(i / K);
+    }
+    free(next);
+    return nerr;
+}
+
+/* ------------------------------------------------------------------------ */
 /* De-duplicated per-partition dispatch                                      */
 /* ------------------------------------------------------------------------ */
 

@@ -250,3 +250,28 @@ def dedup_layout(idx: np.ndarray, E: int, P: int) -> dict:
     slot_src[dst[vt, vk]] = dd_row[vt, idx[vt, vk] // Ep]
     return dict(partition_token_offsets=ptok_off, dedup_row=dd_row, dedup_src_token=dd_src,
                 dedup_topk_idx=dd_idx, slot_src_row=slot_src, num_dedup_rows=int(ptok_off[-1]))
+
+
+def aligned_layout(idx: np.ndarray, E: int, P: int, align: int) -> dict:
+    """Aligned expert runs from the stable-sort permutation: a slot keeps its
+    rank inside its expert, and the runs start at the cumulative sum of the
+    counts rounded up to a multiple of ``align``."""
+    idx = np.asarray(idx, np.int64)
+    T, K = idx.shape
+    Ep = E // P
+    lay = layout(idx, E, P)
+    dst, _ = permutation(idx, E)
+    cnt = lay["num_tokens_per_expert"].astype(np.int64)
+    padded = -(-cnt // align) * align
+    off = np.concatenate([[0], np.cumsum(padded)]).astype(np.int32)
+    flat = idx.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    e_safe = np.where(valid, flat, 0)
+    rank = dst.reshape(-1) - lay["expert_offsets"][e_safe]
+    rows = np.where(valid, off[e_safe] + rank, -1).astype(np.int32)
+    src = np.full(T * K + E * (align - 1), -1, np.int32)
+    src[rows[valid]] = np.nonzero(valid)[0] // K
+    res = dict(lay)
+    res.update(expert_offsets=off, partition_offsets=off[np.arange(P + 1) * Ep].astype(np.int32),
+               dst_row=rows.reshape(T, K), recv_src_token=src)
+    return res

@@ -36,6 +36,9 @@ DISPATCH = [pins.test_bf16_dispatch_rows_are_bitwise_copies,
 DEDUP = [lambda: pins.test_dedup_hand_worked(GOLDEN),
          lambda: pins.test_dedup_random_against_cumsum_and_invariants(1),
          lambda: pins.test_dedup_random_against_cumsum_and_invariants(4)]
+ALIGNED = [lambda: pins.test_aligned_layout_hand_worked(GOLDEN),
+           lambda: pins.test_aligned_layout_random_against_library_routines(1),
+           lambda: pins.test_aligned_layout_random_against_library_routines(4)]
 LL = [lambda: pins.test_ll_layout_hand_worked(GOLDEN),
       lambda: pins.test_ll_layout_random_against_library_routines(1),
       lambda: pins.test_ll_layout_random_against_library_routines(4),
@@ -126,11 +129,23 @@ MUTANTS = [
      "            recv_x[r * H + h] = x[t * H + h];",
      "if (t < 0)\n            t = 0;\n        for (int64_t h = 0; h < H; ++h)\n"
      "            recv_x[r * H + h] = x[t * H + h];", LL),
+    ("aligned runs rounded down", "run += (cnt_e[e] + align - 1) / align * align;",
+     "run += cnt_e[e] / align * align;", ALIGNED),
+    ("aligned runs not padded", "run += (cnt_e[e] + align - 1) / align * align;",
+     "run += cnt_e[e];", ALIGNED),
+    ("aligned partition offsets left unpadded",
+     "    off_e[E] = run;\n    for (int32_t p = 0; p <= P; ++p)\n        off_p[p] = off_e[Ep * p];\n",
+     "    off_e[E] = run;\n", ALIGNED),
+    ("aligned padding rows not marked", "    for (int64_t r = 0; r < R; ++r)\n        src[r] = -1;\n",
+     "", ALIGNED),
+    ("aligned source token from the slot index", "src[dst[i]] = (int32_t)(i / K);",
+     "src[dst[i]] = (int32_t)(i % K);", ALIGNED),
 ]
 
 
 GROUPS = {"E4M3": E4M3, "BF16": BF16, "LAYOUT": LAYOUT, "QUANT": QUANT,
-          "COMBINE": COMBINE, "DISPATCH": DISPATCH, "LL": LL, "DEDUP": DEDUP}
+          "COMBINE": COMBINE, "DISPATCH": DISPATCH, "LL": LL, "DEDUP": DEDUP,
+          "ALIGNED": ALIGNED}
 
 
 def _group_name(checks):

@@ -327,6 +327,81 @@ def test_ll_dispatch_rows_are_copies_and_holes_untouched():
 
 
 # ---------------------------------------------------------------------------
+# expert runs aligned for grouped GEMMs
+# ---------------------------------------------------------------------------
+
+def test_aligned_layout_hand_worked(golden_dir):
+    g = _read_kv(os.path.join(golden_dir, "aligned_layout_hand_worked.txt"))
+    T, K, E, P = (int(g[k][0]) for k in "TKEP")
+    idx = np.array(g["topk_idx"], np.int64).reshape(T, K)
+    for align in (1, 3):
+        got = oracle.aligned_layout(idx, E, P, align)
+        for key in ["num_tokens_per_expert", "num_tokens_per_partition", "is_token_in_partition"]:
+            np.testing.assert_array_equal(np.asarray(got[key]).reshape(-1),
+                                          np.array(g[key], np.int64), err_msg=key)
+        for key in ["expert_offsets", "partition_offsets", "dst_row", "recv_src_token"]:
+            np.testing.assert_array_equal(np.asarray(got[key]).reshape(-1),
+                                          np.array(g["A%d_%s" % (align, key)], np.int32),
+                                          err_msg="%s align=%d" % (key, align))
+        assert got["num_invalid"] == int(g["num_invalid"][0])
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_aligned_layout_random_against_library_routines(seed):
+    rng = np.random.default_rng(1500 + seed)
+    E = int(rng.choice([1, 2, 4, 8, 16, 32, 64, 256]))
+    P = int(rng.choice([d for d in (1, 2, 4, 8) if E % d == 0]))
+    K = int(rng.integers(1, min(E, 8) + 1))
+    T = int(rng.integers(0, 300))
+    c = wl.random_case(T, 8, E, P, K, seed, masked_frac=0.1 * (seed % 3),
+                       invalid_frac=0.05 * (seed % 2), allow_dup=bool(seed % 2),
+                       skew=float(seed % 4), with_y=False)
+    for align in (1, 2, 3, 64, 128):
+        got = oracle.aligned_layout(c.topk_idx, E, P, align)
+        want = bf.aligned_layout(c.topk_idx, E, P, align)
+        for k in want:
+            np.testing.assert_array_equal(np.asarray(got[k]), np.asarray(want[k]),
+                                          err_msg="%s align=%d" % (k, align))
+        # invariants: every run starts on a multiple of align and is the count
+        # rounded up; its first cnt rows hold its tokens, the rest are padding
+        off, cnt = got["expert_offsets"], got["num_tokens_per_expert"]
+        assert np.all(off % align == 0)
+        assert np.all(np.diff(off) == -(-cnt // align) * align)
+        src = got["recv_src_token"]
+        for e in range(E):
+            run = src[off[e]:off[e + 1]]
+            assert np.all(run[:cnt[e]] >= 0) and np.all(run[cnt[e]:] == -1)
+        assert np.all(src[off[E]:] == -1)
+        valid = got["dst_row"] >= 0
+        tok = np.broadcast_to(np.arange(T)[:, None], (T, K))
+        np.testing.assert_array_equal(src[got["dst_row"][valid]], tok[valid])
+
+
+def test_aligned_layout_align_one_is_the_offsets_layout():
+    c = wl.random_case(300, 8, 64, 8, 6, 31, masked_frac=0.1, invalid_frac=0.02,
+                       allow_dup=True, skew=2.0, with_y=False)
+    got = oracle.aligned_layout(c.topk_idx, 64, 8, 1)
+    lay = oracle.layout(c.topk_idx, 64, 8)
+    dst, src = oracle.permutation(c.topk_idx, 64, lay["expert_offsets"])
+    for k in lay:
+        np.testing.assert_array_equal(np.asarray(got[k]), np.asarray(lay[k]), err_msg=k)
+    np.testing.assert_array_equal(got["dst_row"], dst)
+    np.testing.assert_array_equal(got["recv_src_token"], src)
+
+
+def test_aligned_dispatch_rows_are_copies_and_padding_untouched():
+    c = wl.random_case(90, 256, 16, 4, 4, 33, masked_frac=0.1, allow_dup=True)
+    res = oracle.run_aligned(c.topk_idx, c.x_bits, 16, 4, 8, fp8=True)
+    src = res["recv_src_token"]
+    q, s = oracle.quantize(c.x_bits)
+    pad = src < 0
+    assert pad.any() and (~pad).any()
+    np.testing.assert_array_equal(res["recv_x"][~pad], q[src[~pad]])
+    np.testing.assert_array_equal(res["recv_scales"][~pad], s[src[~pad]])
+    assert np.all(res["recv_x"][pad] == 0) and np.all(res["recv_scales"][pad] == 0)
+
+
+# ---------------------------------------------------------------------------
 # de-duplicated per-partition dispatch
 # ---------------------------------------------------------------------------
 
