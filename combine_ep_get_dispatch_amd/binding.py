@@ -24,6 +24,7 @@ EP_DTYPE_FP8_E4M3 = 1
 MAX_EXPERTS = 1024
 MAX_TOPK = 64
 LL_MAX_SLOTS = 8192
+MAX_EXPERT_ALIGNMENT = 1024
 
 
 class EpError(RuntimeError):
@@ -52,6 +53,10 @@ SIGNATURES = {
     "ep_layout_dispatch": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _i32, ctypes.c_int,
                                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                           _vp]),
+    "ep_aligned_rows": (_i64, [_i32, _i32, _i32, _i32]),
+    "ep_layout_dispatch_aligned": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _i32, _i32,
+                                                  ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                  _vp, _vp, _vp, _sz, _vp]),
     "ep_dispatch_dedup": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _i32, ctypes.c_int,
                                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _vp, _vp, _sz, _vp]),
@@ -279,6 +284,68 @@ def layout_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int,
         _ptr(out.recv_x), _ptr(out.recv_scales) if fp8 else None, _ptr(out.recv_src_token),
         _ptr(out.dst_row), _ptr(workspace), workspace.numel(), int(num_cus), _stream(x)),
         "ep_layout_dispatch_cu")
+    return out_layout, out
+
+
+def aligned_rows(num_tokens: int, num_topk: int, num_experts: int, expert_alignment: int) -> int:
+    """ep_aligned_rows: receive rows of layout_dispatch_aligned (0 if rejected)."""
+    return int(lib().ep_aligned_rows(num_tokens, num_topk, num_experts, expert_alignment))
+
+
+def layout_dispatch_aligned(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int,
+                            num_partitions: int, expert_alignment: int,
+                            workspace: torch.Tensor | None = None, fp8: bool = False,
+                            out_layout: Layout | None = None, out: Dispatched | None = None):
+    """ep_layout_dispatch_aligned: layout and dispatch with every expert's run
+    of receive rows padded to a multiple of expert_alignment rows (recv_x,
+    recv_scales and recv_src_token have aligned_rows(...) rows).  Returns
+    (Layout, Dispatched)."""
+    if x.dim() != 2 or topk_idx.dim() != 2:
+        raise ValueError("x must be [T, H] and topk_idx [T, K]")
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    E, P, A = int(num_experts), int(num_partitions), int(expert_alignment)
+    _need(x, torch.bfloat16, "x")
+    _need(topk_idx, torch.int64, "topk_idx", (T, K))
+    R = aligned_rows(T, K, E, A)
+    if R == 0 and T > 0:
+        raise ValueError("expert_alignment %d rejected for T=%d K=%d E=%d" % (A, T, K, E))
+    dev = x.device
+    if workspace is None:
+        workspace = new_workspace(T, K, E, P, dev)
+    _need(workspace, torch.uint8, "workspace")
+    if out_layout is None:
+        out_layout = Layout(torch.empty(E, dtype=torch.int32, device=dev),
+                            torch.empty(P, dtype=torch.int32, device=dev),
+                            torch.empty((T, P), dtype=torch.uint8, device=dev),
+                            torch.empty(E + 1, dtype=torch.int32, device=dev),
+                            torch.empty(P + 1, dtype=torch.int32, device=dev), workspace)
+    else:
+        out_layout.workspace = workspace
+    if out is None:
+        out = Dispatched(
+            torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev),
+            torch.empty((R, H // 128), dtype=torch.float32, device=dev) if fp8 else None,
+            torch.empty(R, dtype=torch.int32, device=dev),
+            torch.empty((T, K), dtype=torch.int32, device=dev))
+    lo = out_layout
+    _need(lo.num_tokens_per_expert, torch.int32, "num_tokens_per_expert", (E,))
+    _need(lo.num_tokens_per_partition, torch.int32, "num_tokens_per_partition", (P,))
+    _need(lo.is_token_in_partition, torch.uint8, "is_token_in_partition", (T, P))
+    _need(lo.expert_offsets, torch.int32, "expert_offsets", (E + 1,))
+    _need(lo.partition_offsets, torch.int32, "partition_offsets", (P + 1,))
+    _need(out.recv_x, torch.uint8 if fp8 else torch.bfloat16, "recv_x", (R, H))
+    if fp8:
+        _need(out.recv_scales, torch.float32, "recv_scales", (R, H // 128))
+    _need(out.recv_src_token, torch.int32, "recv_src_token", (R,))
+    _need(out.dst_row, torch.int32, "dst_row", (T, K))
+    _check(lib().ep_layout_dispatch_aligned(
+        _ptr(x), T, H, _ptr(topk_idx), K, E, P, A, EP_DTYPE_FP8_E4M3 if fp8 else EP_DTYPE_BF16,
+        _ptr(lo.num_tokens_per_expert), _ptr(lo.num_tokens_per_partition),
+        _ptr(lo.is_token_in_partition), _ptr(lo.expert_offsets), _ptr(lo.partition_offsets),
+        _ptr(out.recv_x), _ptr(out.recv_scales) if fp8 else None, _ptr(out.recv_src_token),
+        _ptr(out.dst_row), _ptr(workspace), workspace.numel(), _stream(x)),
+        "ep_layout_dispatch_aligned")
     return out_layout, out
 
 

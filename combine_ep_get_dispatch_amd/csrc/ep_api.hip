@@ -75,7 +75,7 @@ ep_status_t ep_dispatch(const void* x, int32_t num_tokens, int32_t hidden,
     if (workspace_bytes < m.total) return EP_ERR_WORKSPACE;
     return from_hip(ep::launch_dispatch(static_cast<const uint16_t*>(x), T, H, K, fp8, recv_x,
                                         recv_scales, recv_src_token, dst_row, workspace, m, 0,
-                                        static_cast<hipStream_t>(stream)));
+                                        T * K, static_cast<hipStream_t>(stream)));
 }
 
 ep_status_t ep_layout_dispatch_cu(const void* x, int32_t num_tokens, int32_t hidden,
@@ -125,6 +125,59 @@ ep_status_t ep_layout_dispatch(const void* x, int32_t num_tokens, int32_t hidden
                                  num_tokens_per_partition, is_token_in_partition, expert_offsets,
                                  partition_offsets, recv_x, recv_scales, recv_src_token, dst_row,
                                  workspace, workspace_bytes, 0, stream);
+}
+
+int64_t ep_aligned_rows(int32_t num_tokens, int32_t num_topk, int32_t num_experts,
+                        int32_t expert_alignment) {
+    if (check_routing_shape(num_tokens, num_topk, num_experts, 1) != EP_OK) return 0;
+    if (expert_alignment < 1 || expert_alignment > EP_MAX_EXPERT_ALIGNMENT) return 0;
+    const int64_t R = (int64_t)num_tokens * num_topk +
+                      (int64_t)num_experts * (expert_alignment - 1);
+    return R < kMaxRows ? R : 0;
+}
+
+ep_status_t ep_layout_dispatch_aligned(const void* x, int32_t num_tokens, int32_t hidden,
+                                       const int64_t* topk_idx, int32_t num_topk,
+                                       int32_t num_experts, int32_t num_partitions,
+                                       int32_t expert_alignment, ep_dtype_t out_dtype,
+                                       int32_t* num_tokens_per_expert,
+                                       int32_t* num_tokens_per_partition,
+                                       uint8_t* is_token_in_partition, int32_t* expert_offsets,
+                                       int32_t* partition_offsets, void* recv_x,
+                                       float* recv_scales, int32_t* recv_src_token,
+                                       int32_t* dst_row, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    const int32_t T = num_tokens, H = hidden, K = num_topk, E = num_experts, P = num_partitions;
+    ep_status_t st = check_routing_shape(T, K, E, P);
+    if (st != EP_OK) return st;
+    const int64_t R = ep_aligned_rows(T, K, E, expert_alignment);
+    if (R == 0 && T > 0) return EP_ERR_INVALID_ARG;
+    if (expert_alignment < 1 || expert_alignment > EP_MAX_EXPERT_ALIGNMENT)
+        return EP_ERR_INVALID_ARG;
+    if (out_dtype != EP_DTYPE_BF16 && out_dtype != EP_DTYPE_FP8_E4M3) return EP_ERR_INVALID_ARG;
+    const bool fp8 = out_dtype == EP_DTYPE_FP8_E4M3;
+    if (H <= 0 || H % 8 != 0 || (fp8 && H % 128 != 0)) return EP_ERR_INVALID_ARG;
+    if (!num_tokens_per_expert || !num_tokens_per_partition || !expert_offsets ||
+        !partition_offsets || !workspace)
+        return EP_ERR_INVALID_ARG;
+    if (R > 0 && !recv_src_token) return EP_ERR_INVALID_ARG;
+    if (T > 0) {
+        if (!x || !topk_idx || !is_token_in_partition || !recv_x || !dst_row)
+            return EP_ERR_INVALID_ARG;
+        if (fp8 && !recv_scales) return EP_ERR_INVALID_ARG;
+        if (!aligned16(x) || !aligned16(recv_x)) return EP_ERR_INVALID_ARG;
+    }
+    const ep::WsMap m = ep::ws_map(T, K, E, P);
+    if (workspace_bytes < m.total) return EP_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = ep::launch_layout_aligned(topk_idx, T, K, E, P, expert_alignment, workspace, m,
+                                             num_tokens_per_expert, num_tokens_per_partition,
+                                             is_token_in_partition, expert_offsets,
+                                             partition_offsets, recv_src_token, R, s);
+    if (e != hipSuccess) return EP_ERR_HIP;
+    return from_hip(ep::launch_dispatch(static_cast<const uint16_t*>(x), T, H, K, fp8, recv_x,
+                                        recv_scales, recv_src_token, dst_row, workspace, m, 0,
+                                        (int)R, s));
 }
 
 ep_status_t ep_dispatch_dedup(const void* x, int32_t num_tokens, int32_t hidden,

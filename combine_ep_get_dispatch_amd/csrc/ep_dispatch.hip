@@ -656,7 +656,8 @@ __global__ void ll_empty_kernel(int E, int C, int32_t* __restrict__ cnt_e,
 
 hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K, bool fp8, void* recv_x,
                            float* recv_scales, int32_t* recv_src, int32_t* dst_row,
-                           const void* ws, const WsMap& m, int num_cus, hipStream_t s) {
+                           const void* ws, const WsMap& m, int num_cus, int nrows,
+                           hipStream_t s) {
     if (T == 0) return hipSuccess;
     const char* base = static_cast<const char*>(ws);
     const WsHeader* hdr = reinterpret_cast<const WsHeader*>(base);
@@ -666,7 +667,7 @@ hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K, bool fp8, voi
     const size_t lds = fp8 ? sizeof(float) * (size_t)(H / 128) : 0;
     const bool loop = num_cus > 0 && num_cus < T;
     const dim3 grid(loop ? (unsigned)num_cus : (unsigned)T);
-#define EP_D_ARGS x, T, H, K, hdr, rows, recv_x, recv_scales, recv_src, dst_row, nchunk, T * K
+#define EP_D_ARGS x, T, H, K, hdr, rows, recv_x, recv_scales, recv_src, dst_row, nchunk, nrows
     if (fp8 && loop)
         hipLaunchKernelGGL((dispatch_kernel<true, true>), grid, dim3(64 * nw), lds, s, EP_D_ARGS);
     else if (fp8)
@@ -730,7 +731,7 @@ hipError_t launch_layout_dispatch(const uint16_t* x, const int64_t* idx, int T, 
                                      s);
         if (e != hipSuccess) return e;
         return launch_dispatch(x, T, H, K, fp8, recv_x, recv_scales, recv_src, dst_row, ws, m,
-                               num_cus, s);
+                               num_cus, T * K, s);
     }
     hipError_t e = launch_layout_count(idx, T, K, E, P, ws, m, in_part, kCountPre, s);
     if (e != hipSuccess) return e;

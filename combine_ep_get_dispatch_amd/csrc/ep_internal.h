@@ -95,6 +95,15 @@ hipError_t launch_layout(const int64_t* idx, int T, int K, int E, int P, void* w
                          const WsMap& m, int32_t* cnt_e, int32_t* cnt_p, uint8_t* in_part,
                          int32_t* off_e, int32_t* off_p, hipStream_t s);
 
+// The two-launch layout with every expert's run padded to a multiple of
+// align rows (expert_offsets are the padded ones, num_valid in the header the
+// rows in use); the finalize launch also sets recv_src = -1 on every padding
+// row and on rows [used, R).  T = 0 writes zeros and fills recv_src[0, R).
+hipError_t launch_layout_aligned(const int64_t* idx, int T, int K, int E, int P, int align,
+                                 void* ws, const WsMap& m, int32_t* cnt_e, int32_t* cnt_p,
+                                 uint8_t* in_part, int32_t* off_e, int32_t* off_p,
+                                 int32_t* recv_src, int64_t R, hipStream_t s);
+
 // True when launch_layout takes its single-launch form for this shape.
 bool layout_single_launch(int T, int K, int E, int P, const WsMap& m);
 
@@ -118,10 +127,12 @@ constexpr int kDispatchMaxThreads = 1024;
 constexpr int kDispatchChunk = 1024;
 
 // num_cus > 0 (and < T): the CU-budget form, num_cus workgroups looping over
-// the tokens; otherwise one workgroup per token.
+// the tokens; otherwise one workgroup per token.  nrows: receive rows (T*K,
+// or more for an aligned layout); a workspace row outside it is dropped.
 hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K, bool fp8, void* recv_x,
                            float* recv_scales, int32_t* recv_src, int32_t* dst_row,
-                           const void* ws, const WsMap& m, int num_cus, hipStream_t s);
+                           const void* ws, const WsMap& m, int num_cus, int nrows,
+                           hipStream_t s);
 
 // Largest (E + 1) * blocks that workgroup 0 of the one-call layout + dispatch
 // sums (beyond it the call takes the two-step form).

@@ -680,11 +680,16 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
     if (tid == 0) inv[b] = s_err;
 }
 
+// align > 1: every expert's run is padded to a multiple of align rows, and
+// (recv_src given) the padding rows and the rows [used, R) get source -1 --
+// workgroup b marks the padding of experts b, b + nb, ..., and all
+// workgroups stride over the rows past the last run.
 __global__ __launch_bounds__(kLayoutThreads) void layout_finalize_kernel(
     int T, int K, int E, int P, int Ep, int TB, int nb, const int* __restrict__ cnt,
     const int* __restrict__ pcnt, const int* __restrict__ inv, int* __restrict__ rows,
     WsHeader* __restrict__ hdr, int32_t* __restrict__ cnt_e, int32_t* __restrict__ cnt_p,
-    int32_t* __restrict__ off_e, int32_t* __restrict__ off_p) {
+    int32_t* __restrict__ off_e, int32_t* __restrict__ off_p, int align,
+    int32_t* __restrict__ recv_src, int64_t R) {
     extern __shared__ int smem[];
     int* off = smem;          // [E] totals, then exclusive offsets
     int* bef = off + E;       // [E] rows of e in blocks before this one
@@ -701,12 +706,22 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finalize_kernel(
             s_all += c;
             s_bef += (bb < b) ? c : 0;
         }
-        off[e] = s_all;
+        off[e] = align > 1 ? (s_all + align - 1) / align * align : s_all;
         tot[e] = s_all;
         bef[e] = s_bef;
     }
     __syncthreads();
     const int total = block_exclusive_scan(off, E, red);
+
+    if (recv_src) {
+        for (int e = b; e < E; e += nb) {
+            const int r1 = e + 1 < E ? off[e + 1] : total;
+            for (int r = off[e] + tot[e] + tid; r < r1; r += kLayoutThreads) recv_src[r] = -1;
+        }
+        for (int64_t r = total + (int64_t)b * kLayoutThreads + tid; r < R;
+             r += (int64_t)nb * kLayoutThreads)
+            recv_src[r] = -1;
+    }
 
     const int t0 = b * TB;
     const int n = min(TB, T - t0) * K;
@@ -737,6 +752,13 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finalize_kernel(
         hdr->num_valid = total;
         hdr->num_invalid = nerr;
     }
+}
+
+// n ints of p set to v.
+__global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
 }
 
 // T == 0: every count and offset is zero and no slot is invalid.
@@ -897,7 +919,36 @@ hipError_t launch_layout(const int64_t* idx, int T, int K, int E, int P, void* w
     const size_t lds2 = sizeof(int) * 3 * (size_t)E;
     hipLaunchKernelGGL(layout_finalize_kernel, dim3(m.nb), dim3(kLayoutThreads), lds2, s, T, K, E,
                        P, E / P, m.tb, m.nb, cnt, pcnt, inv, rows, hdr, cnt_e, cnt_p, off_e,
-                       off_p);
+                       off_p, 1, nullptr, (int64_t)0);
+    return hipGetLastError();
+}
+
+hipError_t launch_layout_aligned(const int64_t* idx, int T, int K, int E, int P, int align,
+                                 void* ws, const WsMap& m, int32_t* cnt_e, int32_t* cnt_p,
+                                 uint8_t* in_part, int32_t* off_e, int32_t* off_p,
+                                 int32_t* recv_src, int64_t R, hipStream_t s) {
+    char* base = static_cast<char*>(ws);
+    WsHeader* hdr = reinterpret_cast<WsHeader*>(base);
+    if (T == 0) {
+        hipLaunchKernelGGL(layout_empty_kernel, dim3(1), dim3(256), 0, s, E, P, hdr, cnt_e,
+                           cnt_p, off_e, off_p);
+        if (R > 0) {
+            const int64_t blocks = (R + 255) / 256 < 1024 ? (R + 255) / 256 : 1024;
+            hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                               recv_src, R, -1);
+        }
+        return hipGetLastError();
+    }
+    hipError_t err = launch_layout_count(idx, T, K, E, P, ws, m, in_part, kCountPlain, s);
+    if (err != hipSuccess) return err;
+    int* rows = reinterpret_cast<int*>(base + m.rows_off);
+    int* cnt = reinterpret_cast<int*>(base + m.cnt_off);
+    int* pcnt = reinterpret_cast<int*>(base + m.pcnt_off);
+    int* inv = reinterpret_cast<int*>(base + m.inv_off);
+    const size_t lds2 = sizeof(int) * 3 * (size_t)E;
+    hipLaunchKernelGGL(layout_finalize_kernel, dim3(m.nb), dim3(kLayoutThreads), lds2, s, T, K, E,
+                       P, E / P, m.tb, m.nb, cnt, pcnt, inv, rows, hdr, cnt_e, cnt_p, off_e,
+                       off_p, align, recv_src, R);
     return hipGetLastError();
 }
 

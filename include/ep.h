@@ -60,6 +60,7 @@ typedef enum {
 #define EP_MAX_EXPERTS 1024
 #define EP_MAX_TOPK 64
 #define EP_LL_MAX_SLOTS 8192   /* T*K of one ep_low_latency_dispatch call */
+#define EP_MAX_EXPERT_ALIGNMENT 1024   /* of ep_layout_dispatch_aligned */
 
 /*
  * Bytes of device workspace that ep_get_dispatch_layout and ep_dispatch need
@@ -107,8 +108,9 @@ ep_status_t ep_get_dispatch_layout(const int64_t *topk_idx, int32_t num_tokens,
  * rows r >= N get recv_src_token[r] = -1 and their recv_x/recv_scales rows are
  * left untouched.  (A row the workspace would place outside [0, R) -- only
  * possible when the workspace does not come from the matching layout call --
- * is dropped and its slot reported as -1, so no write leaves the buffers.)  Rows are therefore grouped by expert in ascending order and
- * partition p's rows are one contiguous run.
+ * is dropped and its slot reported as -1, so no write leaves the buffers.)
+ * Rows are therefore grouped by expert in ascending order and partition p's
+ * rows are one contiguous run.
  *   out_dtype == EP_DTYPE_BF16:  recv_x is bf16 [R*H], row r a bitwise copy of
  *     x[recv_src_token[r]]; recv_scales is ignored (may be NULL).
  *   out_dtype == EP_DTYPE_FP8_E4M3 (H % 128 == 0): for each token and each
@@ -147,6 +149,55 @@ ep_status_t ep_layout_dispatch(const void *x, int32_t num_tokens, int32_t hidden
                                int32_t *partition_offsets, void *recv_x, float *recv_scales,
                                int32_t *recv_src_token, int32_t *dst_row, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/*
+ * Receive rows of ep_layout_dispatch_aligned: T*K + E*(expert_alignment-1),
+ * enough for any routing; 0 for a shape that call rejects.
+ */
+int64_t ep_aligned_rows(int32_t num_tokens, int32_t num_topk, int32_t num_experts,
+                        int32_t expert_alignment);
+
+/*
+ * Layout and dispatch with every expert's run of receive rows padded to a
+ * multiple of A = expert_alignment rows: the input form of a grouped expert
+ * GEMM whose row tiles must not straddle two experts.  The pages give no such
+ * layout (the nearest is the decode path's fixed-size per-expert buffers,
+ * "DeepSeek releases DeepEP, an efficient communication library for MoE
+ * models", section "DeepEP: Optimizing MoE Communication"); this library's
+ * reading:
+ *   expert_offsets[0] = 0,
+ *   expert_offsets[e+1] = expert_offsets[e] + ceil(cnt_e / A) * A,
+ *   partition_offsets[p] = expert_offsets[p * E/P];
+ *   num_tokens_per_expert (unpadded), num_tokens_per_partition and
+ *   is_token_in_partition as ep_get_dispatch_layout writes them;
+ *   dst_row[t*K+k] = expert_offsets[e] + (rank of (t,k) among expert e's
+ *   valid slots, token-major then slot order), -1 for masked/invalid slots;
+ *   recv_src_token [R] (R = ep_aligned_rows(T, K, E, A)): the source token of
+ *   each row holding one, -1 on the padding rows expert_offsets[e] + cnt_e ..
+ *   expert_offsets[e+1] - 1 and on every row >= expert_offsets[E];
+ *   recv_x [R*H] (bf16, or uint8 E4M3 codes) and recv_scales [R*G]: the rows
+ *   holding a token exactly as ep_dispatch writes them (same copy, same
+ *   quantiser); padding and unused rows are left untouched.
+ * A = 1 gives exactly the outputs of ep_layout_dispatch.  ep_combine takes the
+ * result unchanged with num_rows = R and y laid out like the receive rows.
+ * Other arguments, conditions and errors as ep_layout_dispatch; in addition
+ * 1 <= A <= EP_MAX_EXPERT_ALIGNMENT and R < 2^31 (else EP_ERR_INVALID_ARG).
+ * Three launches on `stream`: the count launch, one that finishes the layout
+ * and marks the padding rows, and the dispatch.  The workspace
+ * (ep_workspace_bytes(T, K, E, P) bytes) afterwards serves
+ * ep_get_device_error.  T may be 0 (counts 0, every row -1).
+ */
+ep_status_t ep_layout_dispatch_aligned(const void *x, int32_t num_tokens, int32_t hidden,
+                                       const int64_t *topk_idx, int32_t num_topk,
+                                       int32_t num_experts, int32_t num_partitions,
+                                       int32_t expert_alignment, ep_dtype_t out_dtype,
+                                       int32_t *num_tokens_per_expert,
+                                       int32_t *num_tokens_per_partition,
+                                       uint8_t *is_token_in_partition, int32_t *expert_offsets,
+                                       int32_t *partition_offsets, void *recv_x,
+                                       float *recv_scales, int32_t *recv_src_token,
+                                       int32_t *dst_row, void *workspace,
+                                       size_t workspace_bytes, void *stream);
 
 /*
  * De-duplicated dispatch: one copy of a token per destination partition

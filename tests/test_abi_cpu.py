@@ -172,6 +172,42 @@ def test_dispatch_dedup_rejects_bad_arguments(buf):
     assert call(wsz=128) == WORKSPACE
 
 
+def test_aligned_rows():
+    L = b.lib()
+    assert L.ep_aligned_rows(4096, 8, 256, 128) == 4096 * 8 + 256 * 127
+    assert L.ep_aligned_rows(4096, 8, 256, 1) == 4096 * 8
+    assert L.ep_aligned_rows(0, 8, 256, 64) == 256 * 63
+    for bad in [(4, 2, 4, 0), (4, 2, 4, 1025), (-1, 2, 4, 8), (4, 0, 4, 8), (4, 5, 4, 8),
+                (2147482648, 1, 1024, 1024), (4, 2, 2048, 8)]:
+        assert L.ep_aligned_rows(*bad) == 0, bad
+
+
+def test_layout_dispatch_aligned_rejects_bad_arguments(buf):
+    L = b.lib()
+    ws = buf(1 << 16)
+    args = {n: buf() for n in ["x", "idx", "ce", "cp", "ip", "oe", "op", "rx", "rs", "src", "dst"]}
+
+    def call(T=4, H=256, K=2, E=4, P=2, A=8, dt=0, w=ws, wsz=1 << 16, **kw):
+        a = dict(args)
+        a.update(kw)
+        return L.ep_layout_dispatch_aligned(a["x"], T, H, a["idx"], K, E, P, A, dt, a["ce"],
+                                            a["cp"], a["ip"], a["oe"], a["op"], a["rx"], a["rs"],
+                                            a["src"], a["dst"], w, wsz, None)
+
+    for name in args:
+        if name == "rs":
+            continue
+        assert call(**{name: None}) == INVALID, name
+    for kw in [dict(w=None), dict(H=0), dict(H=12), dict(dt=2), dict(dt=1, H=136),
+               dict(dt=1, rs=None), dict(E=6, P=4), dict(K=5), dict(T=-3), dict(A=0),
+               dict(A=1025), dict(A=-4), dict(T=2147482648, K=1, E=1024, P=1, A=1024),
+               dict(x=ctypes.c_void_p(0x100008)), dict(rx=ctypes.c_void_p(0x100004))]:
+        assert call(**kw) == INVALID, kw
+    assert call(T=0, A=0) == INVALID
+    assert call(E=2048, P=2) == UNSUPPORTED
+    assert call(wsz=128) == WORKSPACE
+
+
 def test_cu_budget_entry_points_reject_negative_budgets(buf):
     L = b.lib()
     ws = buf(1 << 16)
