@@ -97,6 +97,20 @@ def dedup_algorithmic_bytes(T, H, E, P, K, fp8, nd):
                 total=layout + dispatch + combine)
 
 
+def aligned_algorithmic_bytes(T, H, E, P, K, fp8, n, rows):
+    """The aligned path's bytes: as the offsets path, except that only the n
+    rows holding a token are written (codes or bf16, scales) while the source
+    token goes to every one of the ``rows`` receive rows (padding marked)."""
+    G = H // 128
+    layout = T * K * 8 + T * P + 4 * (E + P + (E + 1) + (P + 1))
+    dispatch = T * H * 2 + T * K * 8 + n * H * (1 if fp8 else 2) + (n * G * 4 if fp8 else 0) \
+        + rows * 4 + T * K * 4
+    R = T * K
+    combine = R * H * 2 + R * 4 + R * 4 + T * H * 2
+    return dict(layout_dispatch_aligned=layout + dispatch, combine=combine,
+                total=layout + dispatch + combine)
+
+
 def kernel_source_hash(kernel):
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
@@ -125,11 +139,12 @@ def pct(a, q):
     return float(np.percentile(np.asarray(a), q)) if len(a) else None
 
 
-def cpu_baseline(wl_case, nbytes, seconds, capacity=None):
+def cpu_baseline(wl_case, nbytes, seconds, capacity=None, align=0):
     """The CPU oracle (single-threaded C) on the same workload, repeated until
     `seconds` of CPU work have accumulated (at least one full pass).  With a
-    capacity it runs the oracle's fixed-capacity path instead (its combine on
-    expert outputs of the layout's shape)."""
+    capacity it runs the oracle's fixed-capacity path instead, with an
+    alignment its aligned path (each combine on expert outputs of the
+    layout's shape)."""
     import oracle
     from combine_ep_get_dispatch_amd import workloads as wl
     passes, t_total = 0, 0.0
@@ -137,9 +152,16 @@ def cpu_baseline(wl_case, nbytes, seconds, capacity=None):
     if capacity is not None:
         y_ll = wl.normal_bf16(300 + wl.CONFIGS[wl_case.name]["c"],
                               (wl_case.E * capacity, wl_case.H))
+    elif align:
+        y_ll = wl.normal_bf16(300 + wl.CONFIGS[wl_case.name]["c"],
+                              (oracle.aligned_rows(wl_case.T, wl_case.K, wl_case.E, align),
+                               wl_case.H))
     while True:
         t0 = time.perf_counter()
-        if capacity is None:
+        if align:
+            oracle.run_aligned(wl_case.topk_idx, wl_case.x_bits, wl_case.E, wl_case.P, align,
+                               wl_case.fp8, y_ll, wl_case.topk_weights)
+        elif capacity is None:
             oracle.run(wl_case.topk_idx, wl_case.x_bits, wl_case.E, wl_case.P, wl_case.fp8,
                        wl_case.y_bits, wl_case.topk_weights)
         else:
@@ -155,8 +177,9 @@ def cpu_baseline(wl_case, nbytes, seconds, capacity=None):
             "sample": "%d full pass(es) of the %s workload (T=%d), %s, "
                       "single-threaded C oracle, %.1f s"
                       % (passes, wl_case.name, wl_case.T,
-                         "layout+dispatch+combine" if capacity is None else
-                         "fixed-capacity (C=%d) dispatch+combine" % capacity, t_total),
+                         ("fixed-capacity (C=%d) dispatch+combine" % capacity) if capacity
+                         else ("aligned (%d rows) layout+dispatch+combine" % align) if align
+                         else "layout+dispatch+combine", t_total),
             "us_per_step": round(t_total / passes * 1e6, 1)}
 
 
@@ -186,6 +209,9 @@ def main():
                     help="time the single-launch fixed-capacity decode path")
     ap.add_argument("--capacity", type=int, default=0,
                     help="rows per expert for --low-latency (default: T)")
+    ap.add_argument("--align", type=int, default=0,
+                    help="time ep_layout_dispatch_aligned with expert runs padded to this "
+                         "many rows + combine")
     args = ap.parse_args()
     if args.config is None:
         args.config = "decode" if args.low_latency else "prefill"
@@ -235,7 +261,13 @@ def main():
         calls = [("ll_dispatch", lambda: ep.low_latency_dispatch(x, idx, E, C, fp8=fp8, out=lld)),
                  ("combine", lambda: ep.combine(y, lld.dst_row, w, out=out))]
     else:
-        y = torch.from_numpy(case.y_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        if args.align:
+            # expert outputs laid out like the aligned receive rows
+            R = ep.aligned_rows(T, K, E, args.align)
+            y = torch.from_numpy(wl.normal_bf16(300 + wl.CONFIGS[args.config]["c"], (R, H))
+                                 .view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            y = torch.from_numpy(case.y_bits.view(np.int16)).to(dev).view(torch.bfloat16)
         ws = ep.new_workspace(T, K, E, P, dev)
         lay = ep.Layout(torch.empty(E, dtype=torch.int32, device=dev),
                         torch.empty(P, dtype=torch.int32, device=dev),
@@ -258,6 +290,9 @@ def main():
                 torch.empty(T * K, dtype=torch.int32, device=dev), disp.dst_row)
             calls = [("dispatch_dedup", lambda: ep.dispatch_dedup(
                 x, idx, E, P, workspace=ws, fp8=fp8, out_layout=lay, out=ddo))]
+        elif args.align:
+            calls = [("layout_dispatch_aligned", lambda: ep.layout_dispatch_aligned(
+                x, idx, E, P, args.align, workspace=ws, fp8=fp8, out_layout=lay, out=disp))]
         elif args.two_calls:
             calls = [("layout", lambda: ep.get_dispatch_layout(idx, E, P, workspace=ws, out=lay)),
                      ("dispatch", lambda: ep.dispatch(x, idx, E, P, ws, fp8=fp8, out=disp))]
@@ -353,6 +388,9 @@ def main():
     elif args.dedup:
         nd = int(ddo.partition_token_offsets[-1].item())
         nb = dedup_algorithmic_bytes(T, H, E, P, K, fp8, nd)
+    elif args.align:
+        n_rows = int((disp.recv_src_token >= 0).sum().item())
+        nb = aligned_algorithmic_bytes(T, H, E, P, K, fp8, n_rows, R)
     else:
         nb = algorithmic_bytes(T, H, E, P, K, fp8)
     value = nb["total"] / (ms_per_step * 1e-3) / 1e9
@@ -439,7 +477,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, nb["total"], args.cpu_seconds, C if args.low_latency else None)
+        cpu = cpu_baseline(case, nb["total"], args.cpu_seconds, C if args.low_latency else None,
+                           args.align)
 
     def q(a):
         return {"p10": round(pct(a, 10), 2), "p50": round(pct(a, 50), 2),
@@ -477,7 +516,8 @@ def main():
                    "cu_budget": args.cu_budget or None,
                    "path": "low_latency" if args.low_latency else
                            ("de-duplicated per partition" if args.dedup else
-                            ("offsets, two calls" if args.two_calls else "offsets, one call"))},
+                            ("offsets, experts aligned to %d rows" % args.align if args.align else
+                             ("offsets, two calls" if args.two_calls else "offsets, one call")))},
         "algorithmic_bytes": nb,
         "breakdown_us": dict({name: q(v) for name, v in call_us.items()},
                              step_with_events=q(tot_us)),

@@ -3,8 +3,8 @@
 Layout, dispatch and combine are captured once with preallocated outputs and
 replayed several times, with eager work and synchronisations between the
 replays; every replay must reproduce the eager results bit for bit.  The
-two-call path, the one-call path (with and without a CU budget) and the
-de-duplicated path are each captured.
+two-call path, the one-call path (with and without a CU budget), the
+de-duplicated path and the aligned path are each captured.
 """
 import numpy as np
 import pytest
@@ -20,7 +20,8 @@ pytestmark = pytest.mark.gpu
 PATHS = [("decode", None, "two_calls"), ("prefill", 1024, "two_calls"),
          ("coarse", 3000, "two_calls"), ("prefill", 1024, "one_call"),
          ("skewed", 3000, "one_call"), ("prefill", 2048, "budget"), ("prefill", 1024, "dedup"),
-         ("coarse", 3000, "dedup")]
+         ("coarse", 3000, "dedup"), ("prefill", 1024, "aligned"), ("decode", None, "aligned")]
+ALIGN = 128
 
 
 @pytest.mark.parametrize("name,T,path", PATHS, ids=["%s-%s-%s" % p for p in PATHS])
@@ -34,6 +35,11 @@ def test_graph_replays_match_eager(name, T, path):
     w = torch.from_numpy(case.topk_weights).to(dev)
     T, K, E, P, H = case.T, case.K, case.E, case.P, case.H
     R = T * K
+    if path == "aligned":
+        # expert outputs laid out like the aligned receive rows
+        R = ep.aligned_rows(T, K, E, ALIGN)
+        y = torch.from_numpy(wl.normal_bf16(960, (R, H)).view(np.int16)).to(dev).view(
+            torch.bfloat16)
 
     def outputs():
         lay = ep.Layout(torch.empty(E, dtype=torch.int32, device=dev),
@@ -70,6 +76,9 @@ def test_graph_replays_match_eager(name, T, path):
         elif path == "dedup":
             ep.dispatch_dedup(x, idx, E, P, workspace=lay.workspace, fp8=case.fp8, out_layout=lay,
                               out=d)
+        elif path == "aligned":
+            ep.layout_dispatch_aligned(x, idx, E, P, ALIGN, workspace=lay.workspace, fp8=case.fp8,
+                                       out_layout=lay, out=d)
         else:
             ep.layout_dispatch(x, idx, E, P, workspace=lay.workspace, fp8=case.fp8,
                                out_layout=lay, out=d, num_cus=budget)
@@ -84,9 +93,11 @@ def test_graph_replays_match_eager(name, T, path):
             tensors += [d.partition_token_offsets, d.recv_topk_idx, d.slot_src_row]
         else:
             n = int(lay.expert_offsets[-1].item())
-        tensors.append(d.recv_x[:n].view(torch.uint8))
+        # rows holding a token (an aligned layout's padding rows are never written)
+        held = (d.recv_src_token[:n] >= 0).nonzero().flatten()
+        tensors.append(d.recv_x[held].view(torch.uint8))
         if case.fp8:
-            tensors.append(d.recv_scales[:n])
+            tensors.append(d.recv_scales[held])
         return [t.cpu().numpy().copy() for t in tensors]
 
     ref = outputs()

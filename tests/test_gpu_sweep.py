@@ -3,8 +3,9 @@
 24 shapes drawn from a fixed generator -- ragged T and H, every kind of E, P
 and K combination the limits allow, masked, invalid and repeated ids, skewed
 routing, bf16 and FP8 -- each run through the two-call path, the one-call
-path, the one-call path under a random CU budget, the de-duplicated path and
-(when T*K allows) the fixed-capacity decode path, and compared with the
+path, the one-call path under a random CU budget, the de-duplicated path, the aligned path
+with a random alignment and (when T*K allows) the fixed-capacity decode
+path, and compared with the
 oracle to the usual bars (bit-exact layout, rows and scales; combine within
 2 bf16 ulp).  The draws are fixed by the seed, so a failure names a
 reproducible case.
@@ -14,6 +15,7 @@ import pytest
 
 from combine_ep_get_dispatch_amd import workloads as wl
 from parity import check_case
+from test_gpu_aligned import check_aligned
 from test_gpu_dedup import check_dedup
 from test_gpu_low_latency import check_ll
 
@@ -35,21 +37,23 @@ def _draw(i):
               allow_dup=bool(rng.integers(0, 2)), skew=float(rng.choice([0.0, 1.0, 3.0])),
               fp8=fp8)
     budget = int(rng.choice([1, 5, 64, 200]))
-    return T, H, E, P, K, 9100 + i, kw, budget
+    align = int(rng.choice([1, 2, 3, 16, 64, 128, 1000]))
+    return T, H, E, P, K, 9100 + i, kw, budget, align
 
 
 SWEEP = [_draw(i) for i in range(24)]
 
 
-@pytest.mark.parametrize("T,H,E,P,K,seed,kw,budget", SWEEP,
+@pytest.mark.parametrize("T,H,E,P,K,seed,kw,budget,align", SWEEP,
                          ids=["s%d_T%d_H%d_E%d_P%d_K%d" % ((i,) + c[:5]) for i, c in enumerate(SWEEP)])
-def test_sweep(T, H, E, P, K, seed, kw, budget):
+def test_sweep(T, H, E, P, K, seed, kw, budget, align):
     case = wl.random_case(T, H, E, P, K, seed, **kw)
     label = "sweep seed=%d" % seed
     check_case(case, label=label)
     check_case(case, label=label, one_call=True)
     check_case(case, label=label, one_call=True, num_cus=budget)
     check_dedup(case, label)
+    check_aligned(case, align, label, y_seed=seed + 2)
     if T * K <= 8192:
         check_ll(case.topk_idx, case.x_bits, case.topk_weights, E, max(1, T // 3), case.fp8,
                  label, y_seed=seed + 1)
