@@ -160,10 +160,10 @@ int64_t ep_aligned_rows(int32_t num_tokens, int32_t num_topk, int32_t num_expert
 /*
  * Layout and dispatch with every expert's run of receive rows padded to a
  * multiple of A = expert_alignment rows: the input form of a grouped expert
- * GEMM whose row tiles must not straddle two experts.  The pages give no such
- * layout (the nearest is the decode path's fixed-size per-expert buffers,
+ * GEMM whose row tiles must not straddle two experts.  The pages give no
+ * receive layout at all (their normal kernels serve training and prefill:
  * "DeepSeek releases DeepEP, an efficient communication library for MoE
- * models", section "DeepEP: Optimizing MoE Communication"); this library's
+ * models", section "Technical Details"); the padding is this library's
  * reading:
  *   expert_offsets[0] = 0,
  *   expert_offsets[e+1] = expert_offsets[e] + ceil(cnt_e / A) * A,

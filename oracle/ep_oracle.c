@@ -406,9 +406,9 @@ void oracle_dispatch_rows_fp8(const uint16_t *x, int32_t T, int32_t H,
  * The expert-major layout of oracle_layout / oracle_permutation with every
  * expert's run padded to a whole number of `align` rows, so that each
  * expert's first row sits on a tile boundary of a grouped expert GEMM.  The
- * pages name no such layout (the decode path's fixed-size per-expert buffers
- * are the nearest: "DeepSeek releases DeepEP ...", section "DeepEP:
- * Optimizing MoE Communication"); this is the plainest reading:
+ * pages give no receive layout at all (their normal kernels serve training
+ * and prefill: "DeepSeek releases DeepEP ...", section "Technical Details");
+ * this is the plainest reading of a padded one:
  *   cnt_e, cnt_p, in_part   as oracle_layout (unpadded counts)
  *   off_e [E+1]  off_e[0] = 0, off_e[e+1] = off_e[e] + ceil(cnt_e[e] / align) * align
  *   off_p [P+1]  off_p[p] = off_e[p * (E/P)]
