@@ -698,6 +698,18 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finalize_kernel(
 
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
+    // The block's packed slots (at most kLayoutEntries) are loaded first:
+    // they do not depend on the sums below.
+    const int t0 = b * TB;
+    const int n = min(TB, T - t0) * K;
+    constexpr int U = kLayoutEntries / kLayoutThreads;
+    static_assert(kLayoutEntries % kLayoutThreads == 0, "whole rounds of slots");
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int j = u * kLayoutThreads + tid;
+        v[u] = j < n ? rows[(int64_t)t0 * K + j] : -1;
+    }
     for (int e = tid; e < E; e += kLayoutThreads) {
         int s_all = 0, s_bef = 0;
 #pragma unroll 8
@@ -723,13 +735,12 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finalize_kernel(
             recv_src[r] = -1;
     }
 
-    const int t0 = b * TB;
-    const int n = min(TB, T - t0) * K;
-    for (int j = tid; j < n; j += kLayoutThreads) {
-        const int vj = rows[(int64_t)t0 * K + j];
-        if (vj >= 0) {
-            const int e = vj >> kRankBits;
-            rows[(int64_t)t0 * K + j] = off[e] + bef[e] + (vj & ((1 << kRankBits) - 1));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int j = u * kLayoutThreads + tid;
+        if (v[u] >= 0) {
+            const int e = v[u] >> kRankBits;
+            rows[(int64_t)t0 * K + j] = off[e] + bef[e] + (v[u] & ((1 << kRankBits) - 1));
         }
     }
 
