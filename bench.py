@@ -209,6 +209,9 @@ def main():
                     help="time the single-launch fixed-capacity decode path")
     ap.add_argument("--capacity", type=int, default=0,
                     help="rows per expert for --low-latency (default: T)")
+    ap.add_argument("--flush-mb", type=int, default=512,
+                    help="also time every step after reading a flush buffer of this many MiB "
+                         "(0: skip)")
     ap.add_argument("--align", type=int, default=0,
                     help="time ep_layout_dispatch_aligned with expert runs padded to this "
                          "many rows + combine")
@@ -340,6 +343,26 @@ def main():
     call_us = {name: [e[i].elapsed_time(e[i + 1]) * 1e3 for e in evs]
                for i, (name, _) in enumerate(calls)}
     tot_us = [e[0].elapsed_time(e[nc]) * 1e3 for e in evs]
+
+    # ---- cold caches: each step after a sweep over a flush buffer -----------
+    # (larger than the L2s and the MALL together, read outside the timed
+    # events, so no input or output of the step is cached when it starts.
+    # The sweep reads, so the caches hold clean lines: a written flush buffer
+    # would charge its own write-back to the step.)
+    if args.flush_mb > 0:
+        flush = torch.ones(args.flush_mb << 20, dtype=torch.uint8, device=dev)
+        n_cold = max(1, args.steps)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_cold)]
+        torch.cuda.synchronize()
+        for i in range(n_cold):
+            flush.sum()
+            cev[i][0].record()
+            step()
+            cev[i][1].record()
+        torch.cuda.synchronize()
+        cold_us = [a.elapsed_time(b) * 1e3 for a, b in cev]
+        del flush
+        log("cold-cache steps: p50 %.2f us" % pct(cold_us, 50))
 
     # ---- the dominant kernel launched back to back on its stream ------------
     # (combine on the offsets path; the single dispatch launch on the decode
@@ -521,6 +544,8 @@ def main():
         "algorithmic_bytes": nb,
         "breakdown_us": dict({name: q(v) for name, v in call_us.items()},
                              step_with_events=q(tot_us)),
+        "cold_cache_us": (dict(q(cold_us), flush_mb=args.flush_mb, steps=len(cold_us))
+                          if args.flush_mb > 0 else None),
         "copy_ceiling_gbs": round(copy_gbs, 1) if copy_gbs else None,
         "pct_of_copy_ceiling": round(100 * value / copy_gbs, 2) if copy_gbs else None,
         "roofline": roofline,
