@@ -27,10 +27,13 @@ __device__ __forceinline__ void store_nt(void* p, const uint4& v) {
 // written through the XCD's L2 instead of staying dirty there.  Used for the
 // receive rows, which the next kernel reads from other XCDs: it leaves less
 // L2 write-back for the end of the kernel (measured faster than ordinary and
-// than non-temporal stores for dispatch's scattered rows).
+// than non-temporal stores for dispatch's scattered rows).  A store of more
+// than 8 bytes needs two wait states on gfx950 before a VALU instruction may
+// overwrite its data registers; the compiler inserts them after the stores it
+// generates but cannot see into inline asm, so the asm carries its own.
 __device__ __forceinline__ void store_wt(void* p, const uint4& v) {
     const u32x4 w = {v.x, v.y, v.z, v.w};
-    asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(w) : "memory");
+    asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" : : "v"(p), "v"(w) : "memory");
 }
 
 // bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 word.
