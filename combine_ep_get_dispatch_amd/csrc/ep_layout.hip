@@ -108,18 +108,28 @@ __device__ int block_exclusive_scan(int* a, int n, int* red) {
 // barrier is shared by the whole workgroup.  mid() runs on every thread
 // between the first and the second barrier (it sees what side() wrote, and
 // what it writes is seen by everything after the call).
+//
+// FINAL = false stops after the second barrier, before the ranks are made
+// block-wide: rnk[j] is then the rank inside its wave's range and the caller
+// adds wcnt[w * E + e] (by then each wave's exclusive prefix over the ranking
+// waves) with w = (j >> 6) / rank_chunks_per_wave(n, nrw) -- one LDS pass and
+// one barrier fewer when the caller reads every rank once anyway.
 struct NoSideWork {
     __device__ void operator()() const {}
 };
 
-template <typename Id, typename Side = NoSideWork, typename Mid = NoSideWork>
+__device__ __forceinline__ int rank_chunks_per_wave(int n, int nrw) {
+    return (((n + 63) >> 6) + nrw - 1) / nrw;
+}
+
+template <bool FINAL = true, typename Id, typename Side = NoSideWork, typename Mid = NoSideWork>
 __device__ void rank_entries(const Id* ids, int n, int E, int ebits, int* wcnt, int* rnk,
                              int* blk_cnt, unsigned* mtab = nullptr, int nrw = kLayoutWaves,
                              Side side = Side(), Mid mid = Mid()) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nchunks = (n + 63) >> 6;
-    const int per = (nchunks + nrw - 1) / nrw;
+    const int per = rank_chunks_per_wave(n, nrw);
     const int c0 = wave < nrw ? wave * per : nchunks;
     const int c1 = min(c0 + per, nchunks);
     int* myw = wcnt + wave * E;
@@ -170,11 +180,13 @@ __device__ void rank_entries(const Id* ids, int n, int E, int ebits, int* wcnt, 
     }
     mid();
     __syncthreads();
-    for (int j = threadIdx.x; j < n; j += kLayoutThreads) {
-        const int e = ids[j];
-        if (e >= 0) rnk[j] += wcnt[((j >> 6) / per) * E + e];
+    if constexpr (FINAL) {
+        for (int j = threadIdx.x; j < n; j += kLayoutThreads) {
+            const int e = ids[j];
+            if (e >= 0) rnk[j] += wcnt[((j >> 6) / per) * E + e];
+        }
+        __syncthreads();
     }
-    __syncthreads();
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves (row
@@ -639,7 +651,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
         }
     };
     if constexpr (PRE) {
-        rank_entries(ids, n, E, ebits, wcnt, rnk, bc, tab, nrw, side, mid);   // ends with a barrier
+        rank_entries<false>(ids, n, E, ebits, wcnt, rnk, bc, tab, nrw, side, mid);   // ends with a barrier
         // One wave scans the block's expert counts and (de-duplicating mode)
         // another its partition counts; the other waves go on with the rows.
         if (tid < 64) {
@@ -664,15 +676,22 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
             }
         }
     } else {
-        rank_entries(ids, n, E, ebits, wcnt, rnk, cnt + (int64_t)b * E, tab, nrw, side);
+        rank_entries<false>(ids, n, E, ebits, wcnt, rnk, cnt + (int64_t)b * E, tab, nrw, side);
     }
-    for (int j = tid; j < n; j += kLayoutThreads) {
-        const int e = ids[j];
-        rows[(int64_t)t0 * K + j] = (e >= 0) ? (e << kRankBits) | rnk[j] : -1;
-        if constexpr (MODE == kCountDedup) {
-            const int w = (j / K) / side_tok;      // the side wave that ranked the token
-            prank[(int64_t)t0 * K + j] =
-                e >= 0 ? prun[w * P + partition_of(e, pmagic)] + (psr[j] & ~kSideTop) : -1;
+    // The packed slots, the in-wave ranks made block-wide on the way; the
+    // waves scanning the block's counts above stay out.
+    const int per = rank_chunks_per_wave(n, nrw);
+    constexpr int busy = MODE == kCountDedup ? 128 : (MODE == kCountPre ? 64 : 0);
+    if (tid >= busy) {
+        for (int j = tid - busy; j < n; j += kLayoutThreads - busy) {
+            const int e = ids[j];
+            rows[(int64_t)t0 * K + j] =
+                (e >= 0) ? (e << kRankBits) | (rnk[j] + wcnt[((j >> 6) / per) * E + e]) : -1;
+            if constexpr (MODE == kCountDedup) {
+                const int w = (j / K) / side_tok;  // the side wave that ranked the token
+                prank[(int64_t)t0 * K + j] =
+                    e >= 0 ? prun[w * P + partition_of(e, pmagic)] + (psr[j] & ~kSideTop) : -1;
+            }
         }
     }
     if constexpr (MODE != kCountDedup)
