@@ -180,7 +180,22 @@ def cpu_baseline(wl_case, nbytes, seconds, capacity=None, align=0):
                          ("fixed-capacity (C=%d) dispatch+combine" % capacity) if capacity
                          else ("aligned (%d rows) layout+dispatch+combine" % align) if align
                          else "layout+dispatch+combine", t_total),
-            "us_per_step": round(t_total / passes * 1e6, 1)}
+            "us_per_step": round(t_total / passes * 1e6, 1),
+            "host": host_info()}
+
+
+def host_info():
+    """The host the CPU baseline ran on: logical CPUs and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu": model}
 
 
 def main():
