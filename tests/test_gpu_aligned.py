@@ -121,6 +121,8 @@ CASES = [
     (1, 8, 4, 2, 2, 128, 80, dict()),
     (50, 256, 1, 1, 1, 64, 81, dict()),
     (9000, 128, 256, 64, 8, 128, 82, dict(masked_frac=0.02, invalid_frac=0.01)),
+    (70, 17536, 64, 8, 8, 64, 87, dict(fp8=True, masked_frac=0.05)),   # waves loop over chunks
+    (66, 18440, 32, 4, 6, 3, 88, dict(allow_dup=True)),
 ]
 
 

@@ -34,6 +34,8 @@ BUDGET_CASES = [
     (9000, 128, 256, 64, 8, 75, dict(masked_frac=0.02), 200),
     (3000, 7168, 256, 64, 8, 76, dict(), 40),        # bf16 rows of the real width
     (50, 256, 16, 4, 2, 77, dict(), 1000),           # budget above the work: no budget
+    (600, 17536, 64, 8, 8, 78, dict(fp8=True), 5),   # waves loop over 18 chunks
+    (66, 18440, 32, 4, 6, 79, dict(), 3),            # the same on the plain dispatch
 ]
 
 

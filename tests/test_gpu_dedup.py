@@ -113,6 +113,8 @@ CASES = [
     (200, 640, 16, 1, 16, 63, dict(fp8=True)),
     (100_000, 16, 4, 2, 1, 64, dict()),
     (9000, 128, 256, 64, 8, 65, dict(masked_frac=0.02, invalid_frac=0.01)),
+    (70, 17536, 64, 8, 8, 69, dict(fp8=True, masked_frac=0.05)),   # waves loop over chunks
+    (66, 18440, 32, 4, 6, 70, dict(allow_dup=True)),
 ]
 
 

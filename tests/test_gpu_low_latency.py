@@ -115,6 +115,8 @@ LL_CASES = [
     (1024, 128, 256, 8, 64, 8, dict(fp8=True, masked_frac=0.02)),    # T*K at the limit
     (40, 8, 4, 2, 3, 9, dict(skew=3.0)),                             # smallest H
     (33, 2048, 1, 1, 40, 10, dict()),                                # one expert
+    (70, 17536, 64, 8, 16, 11, dict(fp8=True, masked_frac=0.05)),    # waves loop over chunks
+    (66, 18440, 32, 6, 20, 12, dict(allow_dup=True)),
 ]
 
 
