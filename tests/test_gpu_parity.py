@@ -50,6 +50,9 @@ GENERIC = [
     (512, 128, 256, 64, 8, 15, dict(masked_frac=0.02, invalid_frac=0.01)),
     (520, 128, 256, 64, 8, 16, dict(masked_frac=0.02, invalid_frac=0.01)),
     (9000, 128, 256, 64, 8, 17, dict(masked_frac=0.02, invalid_frac=0.01)),
+    # few tokens and the largest E: the single-launch layout with more than 64 KiB of LDS
+    (20, 256, 1024, 1024, 64, 20, dict(fp8=True, masked_frac=0.05)),
+    (60, 136, 1024, 256, 32, 21, dict(invalid_frac=0.02)),
     # rows wider than 16 chunks of 1024 channels: waves loop over chunks
     (70, 17536, 64, 8, 8, 18, dict(fp8=True, masked_frac=0.05)),   # 18 chunks, last 128 ch
     (66, 18440, 32, 4, 6, 19, dict(allow_dup=True)),               # 19 chunks, last 8 ch
