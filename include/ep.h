@@ -20,7 +20,9 @@
  * Conventions shared by every entry point:
  *  - Array arguments are device pointers on the current HIP device, row-major
  *    and contiguous, owned by the caller.  The library never allocates or
- *    frees memory; apart from the caller's workspace it keeps no state.
+ *    frees memory; apart from the caller's workspace it keeps no device state
+ *    (its only global is a per-device host flag, set once and thread-safe,
+ *    recording that a kernel's larger dynamic-LDS limit has been raised).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued asynchronously; nothing synchronises except
  *    ep_get_device_error.
