@@ -20,9 +20,16 @@
 // divisions, and the codes come from v_cvt_pk_fp8_f32.  The token's G scales
 // are gathered in LDS and each destination's scale row goes out as one
 // contiguous G*4-byte store.  x is read once (non-temporal: each byte is
-// used once) and quantised once per token, not once per copy; the receive
-// rows are written through L2 (device-scope stores), which measured faster
-// than ordinary and than non-temporal stores here.
+// used once) and quantised once per token, not once per copy; FP8 receive
+// rows are written through L2 (device-scope stores) and bf16 rows
+// non-temporally, each measured fastest for its row size.
+//
+// Kernels: dispatch_kernel (rows from the two-launch layout), the
+// layout-finishing layout_dispatch_kernel (one call: each workgroup sums its
+// token's rows over the count launch's per-block tables), dedup_dispatch_kernel
+// (one copy per token and partition) and ll_dispatch_kernel (fixed capacity
+// per expert, one launch); the first two also have a CU-budget form whose
+// workgroups loop over the tokens.
 #include "ep_internal.h"
 #include "ep_device.h"
 

@@ -7,15 +7,17 @@
 // do not describe it, so the definitions follow include/ep.h.
 //
 // Every slot's rank among the earlier slots of its expert is found inside
-// the workgroup that owns the slot's token: the workgroup's 8 waves take
-// contiguous ranges of its (token, slot) entries and walk them 64 at a time;
-// lanes holding the same expert id are found with one ballot per id bit (AND
-// of the matching ballots), so a slot's rank is its wave's running count
-// (LDS) plus the number of lower lanes in the match -- deterministic and
-// stable, no atomics -- and a prefix over the waves makes it the rank inside
-// the workgroup.  What a workgroup cannot see alone is how many rows the
-// earlier workgroups and the lower experts take.  Two forms provide it, with
-// no atomics or fences between workgroups in either:
+// the workgroup that owns the slot's token: waves take contiguous ranges of
+// its (token, slot) entries and walk them 64 at a time (in the count launch
+// 12 of the 16 waves rank while the other 4 write the partition rows); the
+// lanes holding the same expert id come from a per-wave LDS match table (E <=
+// 256) or from one ballot per id bit (AND of the matching ballots), so a
+// slot's rank is its wave's running count (LDS) plus the number of lower
+// lanes in the match -- deterministic and stable, no atomics between
+// workgroups -- and a prefix over the waves makes it the rank inside the
+// workgroup.  What a workgroup cannot see alone is how many rows the earlier
+// workgroups and the lower experts take.  Three forms provide it, with no
+// atomics or fences between workgroups in any:
 //
 // * fused (one launch, for inputs of at most kFusedMaxBlocks token blocks,
 //   e.g. decode batches): each workgroup stages ALL expert ids in LDS while
@@ -27,11 +29,20 @@
 //   the blocks are few: at 4096 x 8 (16 blocks) it measured 27 us against 14
 //   us for the two launches.
 //
-// * two launches (larger inputs): count writes per-workgroup expert counts
-//   cnt[b][*], partition rows and counts, invalid counts, and for each slot
-//   (expert << 12 | rank in block); finalize sums the count matrix per
-//   workgroup (E * nb ints), scans the totals and rewrites the slots as
-//   receive rows  row = expert_offsets[e] + (rows of e in blocks < b) + rank.
+// * count + finalize (ep_get_dispatch_layout, ep_layout_dispatch_aligned):
+//   count writes per-workgroup expert counts cnt[b][*], partition rows and
+//   counts, invalid counts, and for each slot (expert << 12 | rank in block);
+//   finalize sums the count matrix per workgroup (E * nb ints), scans the
+//   totals (rounded up to the alignment for the aligned layout) and rewrites
+//   the slots as receive rows
+//     row = expert_offsets[e] + (rows of e in blocks < b) + rank.
+//
+// * count + the dispatch launch (ep_layout_dispatch, ep_dispatch_dedup): the
+//   count launch also writes each block's exclusive prefix of its counts over
+//   the experts (and, de-duplicating, the tokens' ranks inside their
+//   partitions and the prefix of the block's partition counts), and every
+//   dispatch workgroup finishes its own token's rows from sums over the
+//   blocks (ep_dispatch.hip).
 #include "ep.h"
 #include "ep_internal.h"
 #include "ep_device.h"
