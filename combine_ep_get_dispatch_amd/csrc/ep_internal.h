@@ -16,10 +16,12 @@ constexpr int kBudgetThreads = 1024;
 constexpr int kBudgetGroups = 4;
 
 // ---------------------------------------------------------------- layout ---
-// The layout kernel gives each workgroup one block of consecutive tokens
-// holding about kLayoutEntries (token, slot) entries, split over 16 waves
-// (two 64-entry chunks per wave: the ranking is a chain of LDS round trips
-// per chunk, and 16 waves measured 0.5 us faster than 8 at 4096 x 8).
+// The layout kernels give each workgroup one block of consecutive tokens
+// holding about kLayoutEntries (token, slot) entries and 16 waves (the
+// ranking is a chain of LDS round trips per 64-entry chunk, so more waves
+// with fewer chunks each finish sooner: 16 measured 0.5 us faster than 8 at
+// 4096 x 8; the count launch ranks with 12 of them, three chunks each at
+// K = 8, while the other 4 write the partition rows).
 constexpr int kLayoutThreads = 1024;
 constexpr int kLayoutWaves = kLayoutThreads / 64;
 constexpr int kLayoutEntries = 2048;
