@@ -37,6 +37,7 @@ DEDUP = [lambda: pins.test_dedup_hand_worked(GOLDEN),
          lambda: pins.test_dedup_random_against_cumsum_and_invariants(1),
          lambda: pins.test_dedup_random_against_cumsum_and_invariants(4)]
 ALIGNED = [lambda: pins.test_aligned_layout_hand_worked(GOLDEN),
+           lambda: pins.test_aligned_layout_exhaustive_small(2, 2),
            lambda: pins.test_aligned_layout_random_against_library_routines(1),
            lambda: pins.test_aligned_layout_random_against_library_routines(4)]
 LL = [lambda: pins.test_ll_layout_hand_worked(GOLDEN),

@@ -346,6 +346,39 @@ def test_aligned_layout_hand_worked(golden_dir):
         assert got["num_invalid"] == int(g["num_invalid"][0])
 
 
+@pytest.mark.parametrize("T,K", [(1, 4), (2, 2), (4, 1), (1, 3)])
+def test_aligned_layout_exhaustive_small(T, K):
+    """Every routing tensor of this shape with ids in {-1, 0, 1, 2, 3} (masked
+    slots and repeated experts included), E = 4, P in {1, 2, 4}, alignments
+    1..3, against ranks from direct pairwise comparison and runs from the
+    counts rounded up by hand."""
+    E = 4
+    n = T * K
+    grid = np.array(np.meshgrid(*[np.arange(-1, E)] * n, indexing="ij")).reshape(n, -1).T
+    batch = grid.reshape(-1, T, K).astype(np.int64)
+    rank = bf.ll_rank_batch(batch, E)
+    for P in (1, 2, 4):
+        for align in (1, 2, 3):
+            for i in range(batch.shape[0]):
+                idx = batch[i]
+                got = oracle.aligned_layout(idx, E, P, align)
+                cnt = np.bincount(idx[idx >= 0], minlength=E)
+                off = [0]
+                for e in range(E):
+                    off.append(off[-1] + (cnt[e] + align - 1) // align * align)
+                off = np.array(off)
+                want_dst = np.where(idx >= 0, off[np.maximum(idx, 0)] + rank[i], -1)
+                assert np.array_equal(got["expert_offsets"], off), (idx, P, align)
+                assert np.array_equal(got["partition_offsets"], off[np.arange(P + 1) * (E // P)])
+                assert np.array_equal(got["dst_row"], want_dst), (idx, P, align)
+                src = np.full(n + E * (align - 1), -1, np.int32)
+                for t in range(T):
+                    for k in range(K):
+                        if want_dst[t, k] >= 0:
+                            src[want_dst[t, k]] = t
+                assert np.array_equal(got["recv_src_token"], src), (idx, P, align)
+
+
 @pytest.mark.parametrize("seed", range(10))
 def test_aligned_layout_random_against_library_routines(seed):
     rng = np.random.default_rng(1500 + seed)
