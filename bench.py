@@ -15,7 +15,12 @@ bf16 weighted combine).
 
 `--low-latency` times the decode path instead: ep_low_latency_dispatch (one
 launch, fixed capacity C per expert, default C = T) -> ep_combine on expert
-outputs laid out like its receive rows.
+outputs laid out like its receive rows.  The other forms each replace the
+layout and dispatch calls of the step: `--dedup` (ep_dispatch_dedup, which also
+writes the layout: one copy per token and destination partition), `--align A`
+(ep_layout_dispatch_aligned, every expert's run padded to a multiple of A rows)
+and `--cu-budget N` (ep_layout_dispatch_cu and ep_combine_cu confined to N
+CUs; with `--overlap-gemm` also timed beside a bf16 GEMM on a second stream).
 
 Prints one JSON line (last line of stdout).  `value` is the effective HBM
 throughput of a step: the algorithmic bytes of the three calls (each input
