@@ -45,7 +45,17 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* In C++ the two enums get int32_t as their fixed underlying type, so that
+ * every int a C caller passes (an unknown status code, a bad dtype that the
+ * call must reject) is a valid value of the parameter's type; the size and
+ * the calling convention are those of the C enums. */
+#ifdef __cplusplus
+#define EP_ENUM_BASE : int32_t
+#else
+#define EP_ENUM_BASE
+#endif
+
+typedef enum EP_ENUM_BASE {
     EP_OK = 0,
     EP_ERR_INVALID_ARG = 1,  /* null pointer, bad size or inconsistent shape */
     EP_ERR_UNSUPPORTED = 2,  /* valid but outside this build's limits       */
@@ -53,7 +63,7 @@ typedef enum {
     EP_ERR_HIP = 4           /* a HIP call or kernel launch failed          */
 } ep_status_t;
 
-typedef enum {
+typedef enum EP_ENUM_BASE {
     EP_DTYPE_BF16 = 0,       /* receive rows are bf16 copies of the tokens  */
     EP_DTYPE_FP8_E4M3 = 1    /* receive rows are OCP E4M3 codes + scales    */
 } ep_dtype_t;
