@@ -47,6 +47,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+X_ROTATION_BYTES = 512 << 20      # twice the MI355X MALL (256 MB)
 METRIC = "dispatch+combine µs/call and effective HBM GB/s (% peak) at 4096×7168 top-8"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {
@@ -232,6 +233,9 @@ def main():
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="also time every step after reading a flush buffer of this many MiB "
                          "(0: skip)")
+    ap.add_argument("--x-copies", type=int, default=0,
+                    help="copies of x the steps rotate over (default: enough for 512 MiB, "
+                         "at most 16; 1 = no rotation)")
     ap.add_argument("--align", type=int, default=0,
                     help="time ep_layout_dispatch_aligned with expert runs padded to this "
                          "many rows + combine")
@@ -268,6 +272,16 @@ def main():
         sys.exit(2)
     idx = torch.from_numpy(case.topk_idx).to(dev)
     x = torch.from_numpy(case.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    # Steps rotate over copies of x that together exceed the 256 MB MALL twice,
+    # so no step finds its tokens left in a cache by an earlier one (the
+    # tokens of a real step are new each time); the routing and the outputs
+    # stay put.
+    n_x = args.x_copies or max(1, min(16, -(-X_ROTATION_BYTES // max(1, T * H * 2))))
+    xs = [x] + [x.clone() for _ in range(n_x - 1)]
+    xcur = [0]
+
+    def xr():
+        return xs[xcur[0]]
     w = torch.from_numpy(case.topk_weights).to(dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     if args.low_latency:
@@ -281,7 +295,7 @@ def main():
             torch.empty(E * C, dtype=torch.int32, device=dev),
             torch.empty((T, K), dtype=torch.int32, device=dev),
             torch.empty(1, dtype=torch.int64, device=dev))
-        calls = [("ll_dispatch", lambda: ep.low_latency_dispatch(x, idx, E, C, fp8=fp8, out=lld)),
+        calls = [("ll_dispatch", lambda: ep.low_latency_dispatch(xr(), idx, E, C, fp8=fp8, out=lld)),
                  ("combine", lambda: ep.combine(y, lld.dst_row, w, out=out))]
     else:
         if args.align:
@@ -312,22 +326,23 @@ def main():
                 torch.empty((T * Kp, K), dtype=torch.int32, device=dev),
                 torch.empty(T * K, dtype=torch.int32, device=dev), disp.dst_row)
             calls = [("dispatch_dedup", lambda: ep.dispatch_dedup(
-                x, idx, E, P, workspace=ws, fp8=fp8, out_layout=lay, out=ddo))]
+                xr(), idx, E, P, workspace=ws, fp8=fp8, out_layout=lay, out=ddo))]
         elif args.align:
             calls = [("layout_dispatch_aligned", lambda: ep.layout_dispatch_aligned(
-                x, idx, E, P, args.align, workspace=ws, fp8=fp8, out_layout=lay, out=disp))]
+                xr(), idx, E, P, args.align, workspace=ws, fp8=fp8, out_layout=lay, out=disp))]
         elif args.two_calls:
             calls = [("layout", lambda: ep.get_dispatch_layout(idx, E, P, workspace=ws, out=lay)),
-                     ("dispatch", lambda: ep.dispatch(x, idx, E, P, ws, fp8=fp8, out=disp))]
+                     ("dispatch", lambda: ep.dispatch(xr(), idx, E, P, ws, fp8=fp8, out=disp))]
         else:
             calls = [("layout_dispatch", lambda: ep.layout_dispatch(
-                x, idx, E, P, workspace=ws, fp8=fp8, out_layout=lay, out=disp,
+                xr(), idx, E, P, workspace=ws, fp8=fp8, out_layout=lay, out=disp,
                 num_cus=args.cu_budget))]
         calls.append(("combine", lambda: ep.combine(y, disp.dst_row, w, out=out,
                                                     num_cus=args.cu_budget)))
     torch.cuda.synchronize()
 
     def step(ev=None):
+        xcur[0] = (xcur[0] + 1) % n_x
         for i, (_, fn) in enumerate(calls):
             if ev is not None:
                 ev[i].record()
@@ -556,7 +571,7 @@ def main():
                                                   % C if args.low_latency else ""),
                    "tokens": T, "hidden": H, "experts": E, "partitions": P, "topk": K,
                    "fp8_dispatch": fp8, "parallelism": "single GPU",
-                   "cu_budget": args.cu_budget or None,
+                   "cu_budget": args.cu_budget or None, "x_copies": n_x,
                    "path": "low_latency" if args.low_latency else
                            ("de-duplicated per partition" if args.dedup else
                             ("offsets, experts aligned to %d rows" % args.align if args.align else

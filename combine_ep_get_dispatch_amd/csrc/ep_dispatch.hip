@@ -10,19 +10,22 @@
 // 64/128-bit instructions, which gfx950 has as global_load/store_dwordx4.
 //
 // Design.  Work is split by SOURCE token, so it is balanced whatever the
-// routing skew: one workgroup per token, one wave per 1024-channel chunk, 16
-// channels per lane -- two 16-byte loads of x per lane and, per destination,
-// one 16-byte store of codes (FP8) or two of bf16, so every destination row is
-// written in whole 1 KiB runs.  The K destination rows come from the layout
+// routing skew: one workgroup per token and one wave per chunk of the row --
+// FP8: 1024 channels, 16 per lane, two 16-byte loads of x per lane and one
+// 16-byte store of codes per destination; bf16: 512 channels, 8 per lane, one
+// 16-byte load and one 16-byte store per destination -- so every destination
+// row is written in whole 1 KiB runs.  The K destination rows come from the layout
 // workspace (lane k loads row(k); the store loop reads it back as a scalar
 // with readlane).  For FP8 a 128-channel group is 8 lanes: its amax is a
 // 3-step xor shuffle, 448/a_c and a_c/448 are correctly rounded fp32
 // divisions, and the codes come from v_cvt_pk_fp8_f32.  The token's G scales
 // are gathered in LDS and each destination's scale row goes out as one
-// contiguous G*4-byte store.  x is read once (non-temporal: each byte is
-// used once) and quantised once per token, not once per copy; FP8 receive
-// rows are written through L2 (device-scope stores) and bf16 rows
-// non-temporally, each measured fastest for its row size.
+// contiguous G*4-byte store.  x is read once (FP8: non-temporal, each byte
+// is used once) and quantised once per token, not once per copy; receive rows
+// are written through L2 (device-scope stores).  The bf16 chunk is half the
+// FP8 one so that a token's copy runs on twice as many waves: its rows are
+// twice as wide, and with 1024-channel chunks the bf16 scatter of 8192 tokens
+// x 7168 channels, top-8, measured 4% slower.
 //
 // Kernels: dispatch_kernel (rows from the two-launch layout), the
 // layout-finishing layout_dispatch_kernel (one call: each workgroup sums its
@@ -41,17 +44,17 @@ __device__ __forceinline__ int partition_of_expert(int e, uint64_t pmagic) {
     return (int)(((uint64_t)(uint32_t)e * pmagic) >> 32);
 }
 
-// One lane's share of one 1024-channel chunk of a token, ready to store.
-// FP8: lane l holds the 16 codes of channels [16l, 16l + 16) of the chunk (its
-// 128-channel group is lanes 8g .. 8g+7; the group's scale goes to s_scale).
-// bf16: lane l holds channels [8l, 8l + 8) and [512 + 8l, 512 + 8l + 8), so
-// every load and store instruction covers 1 KiB of consecutive bytes.
+// One lane's share of one chunk of a token, ready to store.  FP8 (1024-channel
+// chunks): lane l holds the 16 codes of channels [16l, 16l + 16) of the chunk
+// (its 128-channel group is lanes 8g .. 8g+7; the group's scale goes to
+// s_scale).  bf16 (512-channel chunks): lane l holds channels [8l, 8l + 8) in
+// .a, so every load and store instruction covers 1 KiB of consecutive bytes.
 struct ChunkData {
     uint4 a, b;
 };
 
 // The chunk's raw bf16 words as loaded (FP8: 16 channels per lane; bf16:
-// the two 8-channel runs), kept apart from the conversion so that a kernel
+// 8 channels per lane), kept apart from the conversion so that a kernel
 // can issue the loads early and convert once it has waited for them.  The
 // loads are branch-free: a lane past the end of the row loads the row's last
 // 16 bytes instead (always in bounds), and everything downstream ignores it
@@ -69,10 +72,9 @@ __device__ __forceinline__ ChunkData load_raw(const uint16_t* __restrict__ x, in
         d.a = load_nt(xs + hc);                // each byte of x is used once
         d.b = load_nt(xs + hc + 8);
     } else {
-        const int ha = c * kDispatchChunk + lane * 8;
-        const int hb = ha + kDispatchChunk / 2;
-        d.a = *reinterpret_cast<const uint4*>(xs + (ha < H ? ha : H - 8));   // H % 8 == 0
-        d.b = *reinterpret_cast<const uint4*>(xs + (hb < H ? hb : H - 8));
+        const int h0 = c * kDispatchChunkBf16 + lane * 8;
+        d.a = *reinterpret_cast<const uint4*>(xs + (h0 < H ? h0 : H - 8));   // H % 8 == 0
+        d.b = make_uint4(0, 0, 0, 0);
     }
     return d;
 }
@@ -120,8 +122,10 @@ __device__ __forceinline__ ChunkData load_chunk(const uint16_t* __restrict__ x, 
 }
 
 // Store one chunk to the K destination rows held by lanes 0..K-1 of `drow`
-// (-1 = none).  FP8 rows are written through L2 (device-scope stores) and
-// bf16 rows non-temporally: each measured fastest for its row size.
+// (-1 = none).  Rows of both formats are written through L2 (device-scope
+// stores), which measured fastest for each in a steady loop of steps whose
+// tokens are not left in a cache by earlier ones (non-temporal bf16 stores
+// look faster only while the tokens stay cached).
 template <bool FP8>
 __device__ __forceinline__ void store_chunk(const ChunkData& d, int H, int K, int c, int drow,
                                             void* __restrict__ recv_x) {
@@ -135,14 +139,12 @@ __device__ __forceinline__ void store_chunk(const ChunkData& d, int H, int K, in
             if (act) store_wt(static_cast<uint8_t*>(recv_x) + (int64_t)r * H + h0, d.a);
         }
     } else {
-        const int ha = c * kDispatchChunk + lane * 8;
-        const int hb = ha + kDispatchChunk / 2;
+        const int h0 = c * kDispatchChunkBf16 + lane * 8;
+        const bool act = h0 < H;
         for (int k = 0; k < K; ++k) {
             const int r = __builtin_amdgcn_readlane(drow, k);
             if (r < 0) continue;
-            uint16_t* dst = static_cast<uint16_t*>(recv_x) + (int64_t)r * H;
-            if (ha < H) store_nt(dst + ha, d.a);
-            if (hb < H) store_nt(dst + hb, d.b);
+            if (act) store_wt(static_cast<uint16_t*>(recv_x) + (int64_t)r * H + h0, d.a);
         }
     }
 }
@@ -676,7 +678,7 @@ hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K, bool fp8, voi
     const char* base = static_cast<const char*>(ws);
     const WsHeader* hdr = reinterpret_cast<const WsHeader*>(base);
     const int* rows = reinterpret_cast<const int*>(base + m.rows_off);
-    const int nchunk = (H + kDispatchChunk - 1) / kDispatchChunk;
+    const int nchunk = (H + dispatch_chunk(fp8) - 1) / dispatch_chunk(fp8);
     const int nw = nchunk < kDispatchMaxThreads / 64 ? nchunk : kDispatchMaxThreads / 64;
     const size_t lds = fp8 ? sizeof(float) * (size_t)(H / 128) : 0;
     const bool loop = num_cus > 0 && num_cus < T;
@@ -702,7 +704,7 @@ hipError_t launch_ll_dispatch(const uint16_t* x, const int64_t* idx, int T, int 
                               int C, bool fp8, int32_t* cnt_e, void* recv_x, float* recv_scales,
                               int32_t* recv_src, int32_t* dst_row, int64_t* num_invalid,
                               hipStream_t s) {
-    const int nchunk = (H + kDispatchChunk - 1) / kDispatchChunk;
+    const int nchunk = (H + dispatch_chunk(fp8) - 1) / dispatch_chunk(fp8);
     const int nw = kLlWaves;
     static_assert(kLlWaves * 64 <= kDispatchMaxThreads, "block too large");
     const size_t lds = ll_dispatch_lds_bytes(E, H, fp8);
@@ -730,7 +732,7 @@ hipError_t launch_layout_dispatch(const uint16_t* x, const int64_t* idx, int T, 
                                   int32_t* off_e, int32_t* off_p, void* recv_x,
                                   float* recv_scales, int32_t* recv_src, int32_t* dst_row,
                                   int num_cus, hipStream_t s) {
-    const int nchunk = (H + kDispatchChunk - 1) / kDispatchChunk;
+    const int nchunk = (H + dispatch_chunk(fp8) - 1) / dispatch_chunk(fp8);
     const int nw = nchunk < kDispatchMaxThreads / 64 ? nchunk : kDispatchMaxThreads / 64;
     // The finishing sums are one round of loads per token workgroup and a
     // bounded amount of work for workgroup 0; other shapes (and those with a
@@ -809,7 +811,7 @@ hipError_t launch_dispatch_dedup(const uint16_t* x, const int64_t* idx, int T, i
     const int* ppre = reinterpret_cast<const int*>(base + m.ppre_off);
     const int* prank = reinterpret_cast<const int*>(base + m.prank_off);
     const int* rows = reinterpret_cast<const int*>(base + m.rows_off);
-    const int nchunk = (H + kDispatchChunk - 1) / kDispatchChunk;
+    const int nchunk = (H + dispatch_chunk(fp8) - 1) / dispatch_chunk(fp8);
     const int nw = nchunk < kDispatchMaxThreads / 64 ? nchunk : kDispatchMaxThreads / 64;
     // Enough threads for at least one lane per term group, and segments of S
     // lanes (a power of two, <= 64, no wider than the blocks need).

@@ -123,10 +123,15 @@ hipError_t launch_layout_count(const int64_t* idx, int T, int K, int E, int P, v
                                const WsMap& m, uint8_t* in_part, int mode, hipStream_t s);
 
 // ---------------------------------------------------------------- dispatch --
-// One workgroup per token, one wave per 1024-channel chunk (16 channels per
-// lane), at most 16 waves; wider rows loop over their chunks.
+// One workgroup per token, one wave per chunk of the row, at most 16 waves;
+// wider rows loop over their chunks.  FP8: 1024-channel chunks (16 channels
+// per lane); bf16: 512-channel chunks (8 channels per lane).
 constexpr int kDispatchMaxThreads = 1024;
 constexpr int kDispatchChunk = 1024;
+constexpr int kDispatchChunkBf16 = 512;
+__host__ __device__ constexpr int dispatch_chunk(bool fp8) {
+    return fp8 ? kDispatchChunk : kDispatchChunkBf16;
+}
 
 // num_cus > 0 (and < T): the CU-budget form, num_cus workgroups looping over
 // the tokens; otherwise one workgroup per token.  nrows: receive rows (T*K,
