@@ -53,9 +53,17 @@ GENERIC = [
     # few tokens and the largest E: the single-launch layout with more than 64 KiB of LDS
     (20, 256, 1024, 1024, 64, 20, dict(fp8=True, masked_frac=0.05)),
     (60, 136, 1024, 256, 32, 21, dict(invalid_frac=0.02)),
-    # rows wider than 16 chunks of 1024 channels: waves loop over chunks
+    # rows wider than 16 chunks (1024 channels FP8, 512 bf16): waves loop over chunks
     (70, 17536, 64, 8, 8, 18, dict(fp8=True, masked_frac=0.05)),   # 18 chunks, last 128 ch
-    (66, 18440, 32, 4, 6, 19, dict(allow_dup=True)),               # 19 chunks, last 8 ch
+    (66, 18440, 32, 4, 6, 19, dict(allow_dup=True)),               # 37 chunks, last 8 ch
+    # the two-launch layout (more than two blocks of 2048 slots) with K a power of two
+    # up to 16 and P a multiple of 16 (membership rows in 16-byte stores), several
+    # slots of a token in one partition
+    (3000, 256, 64, 64, 4, 22, dict(masked_frac=0.05, invalid_frac=0.01)),
+    (5000, 128, 64, 32, 2, 23, dict(allow_dup=True)),
+    (9000, 128, 32, 16, 1, 24, dict(masked_frac=0.1)),
+    (600, 256, 256, 64, 16, 25, dict(allow_dup=True, invalid_frac=0.02)),
+    (1000, 264, 96, 48, 8, 26, dict(masked_frac=0.1)),
 ]
 
 
