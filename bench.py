@@ -4,7 +4,9 @@ One step = the whole path on one batch: ep_layout_dispatch (the layout and
 the dispatch in one call, two kernel launches) -> ep_combine, on seeded
 synthetic routing and activations that are resident in HBM before timing
 starts (`--two-calls` times ep_get_dispatch_layout -> ep_dispatch ->
-ep_combine instead).  The default workload is the
+ep_combine instead).  Successive steps take their tokens from different
+copies of x, together more than twice the 256 MB MALL, so that no step
+reads tokens an earlier one left in a cache.  The default workload is the
 prefill configuration (4096 tokens x 7168 hidden, top-8 of 256 experts with
 group-limited gating, 64 partitions, FP8 E4M3 dispatch with per-128 scales,
 bf16 weighted combine).
