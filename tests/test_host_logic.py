@@ -27,3 +27,28 @@ def test_bench_refuses_more_than_one_gpu():
         assert proc.returncode == 2, (args, proc.returncode, proc.stderr)
         assert "one GPU" in proc.stderr
         assert proc.stdout == ""
+
+
+def test_bench_byte_model_matches_the_published_table():
+    """bench.py's algorithmic bytes per step (what `value` divides by the step
+    time) reproduce the byte model's table of the five workloads: layout,
+    dispatch and combine bytes as printed there, each within one unit of its
+    last printed digit."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from combine_ep_get_dispatch_amd import workloads as wl
+    # config -> (layout, dispatch, combine) bytes and the rounding step of each figure
+    table = {
+        "tiny": ((1.4e3, 100.4e3, 99.3e3), (0.1e3, 0.1e3, 0.1e3)),
+        "decode": ((14e3, 9.42e6, 16.52e6), (1e3, 0.01e6, 0.01e6)),
+        "prefill": ((0.53e6, 301.47e6, 528.74e6), (0.01e6, 0.01e6, 0.01e6)),
+        "skewed": ((1.05e6, 1058.0e6, 1057.5e6), (0.01e6, 0.1e6, 0.1e6)),
+        "coarse": ((0.79e6, 806.4e6, 805.8e6), (0.01e6, 0.1e6, 0.1e6)),
+    }
+    for name, (want, step) in table.items():
+        c = wl.CONFIGS[name]
+        got = bench.algorithmic_bytes(c["T"], c["H"], c["E"], c["P"], c["K"], c["fp8"])
+        for part, w, s in zip(("layout", "dispatch", "combine"), want, step):
+            assert abs(got[part] - w) < s, (name, part, got[part], w)
+        assert got["total"] == got["layout"] + got["dispatch"] + got["combine"]
+    assert bench.algorithmic_bytes(4096, 7168, 256, 64, 8, True)["total"] == 830_736_904
