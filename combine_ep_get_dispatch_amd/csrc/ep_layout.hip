@@ -59,41 +59,51 @@ __device__ __forceinline__ int stored_id(int64_t v, int E) {
     return (v >= 0 && v < E) ? (int)v : (v == -1 ? -1 : -2);
 }
 
-// Exclusive scan of a[0..n) in LDS by the whole workgroup; returns the total
-// to every thread.  `red` is kLayoutWaves + 1 ints of LDS scratch.
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (row
+// shifts by 1, 2, 4, 8 inside each 16-lane row, then the row broadcasts of
+// lanes 15 and 31); no LDS traffic.  Lanes a move has no source for take 0.
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+    const int lane = threadIdx.x & 63;
+    int t;
+    t = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    if ((lane & 15) >= 1) x += t;
+    t = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    if ((lane & 15) >= 2) x += t;
+    t = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    if ((lane & 15) >= 4) x += t;
+    t = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    if ((lane & 15) >= 8) x += t;
+    t = __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
+    if (lane & 16) x += t;
+    t = __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
+    if (lane & 32) x += t;
+    return x;
+}
+
+// Exclusive scan of a[0..n) in LDS, called by the whole workgroup; returns
+// the total to every thread.  Wave 0 alone scans: lane l sums its
+// ceil(n / 64) consecutive values, a DPP inclusive sum joins the lanes, and
+// the lane writes its values' exclusive prefixes back; one barrier publishes
+// them and the total (`red`: one int of LDS scratch).
 __device__ int block_exclusive_scan(int* a, int n, int* red) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int per = (n + kLayoutThreads - 1) / kLayoutThreads;
-    const int i0 = tid * per;
-    const int i1 = min(i0 + per, n);
-    int local = 0;
-    for (int i = i0; i < i1; ++i) local += a[i];
-    int inc = local;   // inclusive scan of `local` across the wave
-    for (int d = 1; d < 64; d <<= 1) {
-        const int up = __shfl_up(inc, d);
-        if (lane >= d) inc += up;
-    }
-    if (lane == 63) red[wave] = inc;
-    __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int w = 0; w < kLayoutWaves; ++w) {
-            const int v = red[w];
-            red[w] = run;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const int per = (n + 63) >> 6;
+        const int i0 = lane * per;
+        const int i1 = min(i0 + per, n);
+        int local = 0;
+        for (int i = i0; i < i1; ++i) local += a[i];
+        const int inc = wave_inclusive_sum(local);
+        int run = inc - local;
+        for (int i = i0; i < i1; ++i) {
+            const int v = a[i];
+            a[i] = run;
             run += v;
         }
-        red[kLayoutWaves] = run;
+        if (lane == 63) red[0] = inc;
     }
     __syncthreads();
-    int run = red[wave] + inc - local;
-    for (int i = i0; i < i1; ++i) {
-        const int v = a[i];
-        a[i] = run;
-        run += v;
-    }
-    const int total = red[kLayoutWaves];
-    __syncthreads();
-    return total;
+    return red[0];
 }
 
 // Stable ranks of the workgroup's own entries ids[0..n) (stored ids, < 0 =
@@ -198,27 +208,6 @@ __device__ void rank_entries(const Id* ids, int n, int E, int ebits, int* wcnt, 
         }
         __syncthreads();
     }
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (row
-// shifts by 1, 2, 4, 8 inside each 16-lane row, then the row broadcasts of
-// lanes 15 and 31); no LDS traffic.  Lanes a move has no source for take 0.
-__device__ __forceinline__ int wave_inclusive_sum(int x) {
-    const int lane = threadIdx.x & 63;
-    int t;
-    t = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
-    if ((lane & 15) >= 1) x += t;
-    t = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
-    if ((lane & 15) >= 2) x += t;
-    t = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
-    if ((lane & 15) >= 4) x += t;
-    t = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
-    if ((lane & 15) >= 8) x += t;
-    t = __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
-    if (lane & 16) x += t;
-    t = __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
-    if (lane & 32) x += t;
-    return x;
 }
 
 // One wave writes the block's expert counts cnt[0..E) and their exclusive
@@ -490,7 +479,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_fused_kernel(
     int* rnk = wcnt + kLayoutWaves * E;            // [kLayoutEntries]
     int* pc = rnk + kLayoutEntries;                // [P]
     int16_t* ids = reinterpret_cast<int16_t*>(pc + P);   // [T*K] stored ids
-    __shared__ int red[kLayoutWaves + 1];
+    __shared__ int red[1];
     __shared__ int s_err;
 
     const int tid = threadIdx.x;
@@ -724,7 +713,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finalize_kernel(
     int* off = smem;          // [E] totals, then exclusive offsets
     int* bef = off + E;       // [E] rows of e in blocks before this one
     int* tot = bef + E;       // [E] totals (kept for the outputs)
-    __shared__ int red[kLayoutWaves + 1];
+    __shared__ int red[1];
 
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
