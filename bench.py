@@ -147,12 +147,13 @@ def pct(a, q):
     return float(np.percentile(np.asarray(a), q)) if len(a) else None
 
 
-def cpu_baseline(wl_case, nbytes, seconds, capacity=None, align=0):
+def cpu_baseline(wl_case, nbytes, seconds, capacity=None, align=0, dedup=False):
     """The CPU oracle (single-threaded C) on the same workload, repeated until
     `seconds` of CPU work have accumulated (at least one full pass).  With a
     capacity it runs the oracle's fixed-capacity path instead, with an
     alignment its aligned path (each combine on expert outputs of the
-    layout's shape)."""
+    layout's shape), with dedup its de-duplicated dispatch and the combine
+    over the offsets layout's rows."""
     import oracle
     from combine_ep_get_dispatch_amd import workloads as wl
     passes, t_total = 0, 0.0
@@ -169,6 +170,10 @@ def cpu_baseline(wl_case, nbytes, seconds, capacity=None, align=0):
         if align:
             oracle.run_aligned(wl_case.topk_idx, wl_case.x_bits, wl_case.E, wl_case.P, align,
                                wl_case.fp8, y_ll, wl_case.topk_weights)
+        elif dedup:
+            res = oracle.run_dedup(wl_case.topk_idx, wl_case.x_bits, wl_case.E, wl_case.P,
+                                   wl_case.fp8)
+            oracle.combine(wl_case.y_bits, res["dst_row"], wl_case.topk_weights)
         elif capacity is None:
             oracle.run(wl_case.topk_idx, wl_case.x_bits, wl_case.E, wl_case.P, wl_case.fp8,
                        wl_case.y_bits, wl_case.topk_weights)
@@ -187,6 +192,7 @@ def cpu_baseline(wl_case, nbytes, seconds, capacity=None, align=0):
                       % (passes, wl_case.name, wl_case.T,
                          ("fixed-capacity (C=%d) dispatch+combine" % capacity) if capacity
                          else ("aligned (%d rows) layout+dispatch+combine" % align) if align
+                         else "de-duplicated layout+dispatch, combine" if dedup
                          else "layout+dispatch+combine", t_total),
             "us_per_step": round(t_total / passes * 1e6, 1),
             "host": host_info()}
@@ -538,7 +544,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, nb["total"], args.cpu_seconds, C if args.low_latency else None,
-                           args.align)
+                           args.align, args.dedup)
 
     def q(a):
         return {"p10": round(pct(a, 10), 2), "p50": round(pct(a, 50), 2),

@@ -52,3 +52,17 @@ def test_bench_byte_model_matches_the_published_table():
             assert abs(got[part] - w) < s, (name, part, got[part], w)
         assert got["total"] == got["layout"] + got["dispatch"] + got["combine"]
     assert bench.algorithmic_bytes(4096, 7168, 256, 64, 8, True)["total"] == 830_736_904
+
+
+def test_cpu_baseline_runs_the_path_being_timed():
+    """bench.py's CPU baseline times the oracle of the same path as the GPU
+    step: offsets, de-duplicated, aligned or fixed capacity."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from combine_ep_get_dispatch_amd import workloads as wl
+    case = wl.make("tiny")
+    for kw, words in [({}, "layout+dispatch+combine"), ({"dedup": True}, "de-duplicated"),
+                      ({"align": 8}, "aligned (8 rows)"), ({"capacity": 16}, "fixed-capacity (C=16)")]:
+        r = bench.cpu_baseline(case, 1000, 0.0, **kw)
+        assert r["kind"] == "oracle" and r["cores"] == 1 and r["value"] > 0
+        assert words in r["sample"], (kw, r["sample"])
