@@ -251,6 +251,13 @@ def main():
     if args.config is None:
         args.config = "decode" if args.low_latency else "prefill"
 
+    forms = [f for f, on in [("--two-calls", args.two_calls), ("--dedup", args.dedup),
+                             ("--align", args.align), ("--low-latency", args.low_latency)] if on]
+    if len(forms) > 1 or (args.cu_budget and forms):
+        print("bench.py times one path at a time, and --cu-budget only the one-call path: got %s"
+              % " ".join(forms + (["--cu-budget"] if args.cu_budget else [])), file=sys.stderr)
+        sys.exit(2)
+
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build models the all-to-all's "

@@ -66,3 +66,15 @@ def test_cpu_baseline_runs_the_path_being_timed():
         r = bench.cpu_baseline(case, 1000, 0.0, **kw)
         assert r["kind"] == "oracle" and r["cores"] == 1 and r["value"] > 0
         assert words in r["sample"], (kw, r["sample"])
+
+
+def test_bench_refuses_paths_it_cannot_time_together():
+    """One path per run, and the CU budget only on the one-call path: other
+    combinations exit with a message before touching a device."""
+    for args in (["--two-calls", "--cu-budget", "8"], ["--dedup", "--align", "8"],
+                 ["--low-latency", "--two-calls"], ["--align", "64", "--cu-budget", "4"]):
+        proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + args,
+                              capture_output=True, text=True, timeout=120)
+        assert proc.returncode == 2, (args, proc.returncode, proc.stderr)
+        assert "one path at a time" in proc.stderr
+        assert proc.stdout == ""
