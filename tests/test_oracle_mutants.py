@@ -28,6 +28,9 @@ LAYOUT = [lambda: pins.test_layout_hand_worked(GOLDEN),
           pins.test_layout_invalid_ids_are_masked_and_counted]
 QUANT = [pins.test_quantize_matches_numpy_steps_and_invariants,
          pins.test_fp8_dispatch_rows_are_quantised_tokens]
+# The quantiser's two divisions, pinned without the numpy restatement of its steps.
+QUANT_EXACT = [lambda: pins.test_quantize_hand_worked_scale_groups(GOLDEN),
+               pins.test_quantize_exact_rational]
 COMBINE = [lambda: pins.test_combine_hand_worked(GOLDEN), pins.test_combine_exact_rational_small,
            pins.test_combine_closed_forms, pins.test_combine_identity_expert_and_fp64_bound,
            pins.test_combine_rounding_sensitive_cases]
@@ -91,7 +94,9 @@ MUTANTS = [
     ("unused rows not marked", "        src[r] = -1;\n    free(next);", "    free(next);", LAYOUT),
     ("scale inverted", "s[t * G + g] = ac / 448.0f;", "s[t * G + g] = 448.0f / ac;", QUANT),
     ("quantiser multiplies by a reciprocal", "float inv = 448.0f / ac;",
-     "float inv = 448.0f * (1.0f / ac);", QUANT),
+     "float inv = 448.0f * (1.0f / ac);", QUANT_EXACT),
+    ("scale multiplies by a reciprocal", "s[t * G + g] = ac / 448.0f;",
+     "s[t * G + g] = ac * (1.0f / 448.0f);", QUANT_EXACT),
     ("amax floor dropped", "float ac = (a > 1e-4f) ? a : 1e-4f;", "float ac = a;", QUANT),
     ("amax without abs", "float v = fabsf(bf16_to_f32(x[t * H + 128 * g + j]));",
      "float v = bf16_to_f32(x[t * H + 128 * g + j]);", QUANT),
@@ -144,7 +149,7 @@ MUTANTS = [
 ]
 
 
-GROUPS = {"E4M3": E4M3, "BF16": BF16, "LAYOUT": LAYOUT, "QUANT": QUANT,
+GROUPS = {"E4M3": E4M3, "BF16": BF16, "LAYOUT": LAYOUT, "QUANT": QUANT, "QUANT_EXACT": QUANT_EXACT,
           "COMBINE": COMBINE, "DISPATCH": DISPATCH, "LL": LL, "DEDUP": DEDUP,
           "ALIGNED": ALIGNED}
 

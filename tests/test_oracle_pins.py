@@ -12,6 +12,7 @@
   combine.
 """
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -585,6 +586,80 @@ def test_quantize_matches_numpy_steps_and_invariants():
     zs = np.float32(np.float32(1e-4) / np.float32(448.0))
     assert s[0, 0] == zs and s[1, 1] == zs
     assert np.all(qg[0, 0] == 0x00) and np.all(qg[1, 1] == 0x80)
+
+
+def _f32_bits(v) -> int:
+    return int(np.array([v], np.float32).view(np.uint32)[0])
+
+
+_FLOOR = Fraction(float(np.float32(1e-4)))        # a_c = max(a, 1e-4f): the fp32 value of 1e-4
+
+
+def test_quantize_hand_worked_scale_groups(golden_dir):
+    """Groups whose codes and scales were worked out by hand with exact arithmetic
+    (tests/golden/fp8_scale_hand_worked.txt): inv = RN32(448 / a_c) and
+    s = RN32(a_c / 448) computed any other way -- for instance as products with a
+    rounded reciprocal -- change a code or a scale there.  The fixture's own inv,
+    scale and codes are re-derived from exact rationals, so a slip in the hand
+    arithmetic fails too."""
+    groups = {}
+    for line in open(os.path.join(golden_dir, "fp8_scale_hand_worked.txt")):
+        f = line.split()
+        if not f or f[0].startswith("#"):
+            continue
+        g = groups.setdefault(int(f[1]), {"ch": [], "inv": None, "scale": None})
+        if f[2] == "ch":
+            g["ch"].append((int(f[3]), int(f[5], 16), int(f[7], 16)))
+        else:
+            g["inv"], g["scale"] = int(f[3], 16), int(f[5], 16)
+    ng = len(groups)
+    xb = np.zeros((1, 128 * ng), np.uint16)
+    want_q = np.zeros((1, 128 * ng), np.uint8)
+    want_s = np.zeros(ng, np.uint32)
+    for gi, g in groups.items():
+        for ch, xbits, code in g["ch"]:
+            xb[0, 128 * gi + ch] = xbits
+            want_q[0, 128 * gi + ch] = code
+        want_s[gi] = g["scale"]
+        # the hand arithmetic, redone with exact rationals
+        xs = [Fraction(float(bf.bf16_bits_to_f32([xbits])[0])) for _, xbits, _ in g["ch"]]
+        ac = max(max(abs(v) for v in xs), _FLOOR)
+        inv = bf.f32_round(Fraction(448) / ac)
+        assert _f32_bits(inv) == g["inv"]
+        assert _f32_bits(bf.f32_round(ac / 448)) == g["scale"]
+        for v, (_, _, code) in zip(xs, g["ch"]):
+            assert int(bf.e4m3_nearest([bf.f32_round(v * Fraction(inv))])[0]) == code
+    q, s = oracle.quantize(xb)
+    np.testing.assert_array_equal(q, want_q)
+    np.testing.assert_array_equal(s.reshape(-1).view(np.uint32), want_s)
+
+
+def test_quantize_exact_rational():
+    """Scales and codes of many groups against exact arithmetic: the two
+    divisions as correctly rounded quotients of exact rationals, each code from
+    the product x * inv (exact in float64: an 8-bit times a 24-bit significand)
+    rounded once to fp32, then the exhaustive nearest-code encoder.  The group
+    maxima span seven decades, with many just above and below the 1e-4 floor."""
+    rng = np.random.default_rng(17)
+    T = 192
+    xf = rng.standard_normal((T, 128), dtype=np.float32)
+    mag = np.where(np.arange(T) % 2 == 0,
+                   10.0 ** rng.uniform(-6.0, 2.0, T),            # anywhere
+                   10.0 ** rng.uniform(-4.3, -3.7, T))           # around the floor
+    xf *= (mag / np.abs(xf).max(axis=1))[:, None].astype(np.float32)
+    xb = wl.bf16_bits_from_f32(xf)
+    q, s = oracle.quantize(xb)
+    x = bf.bf16_bits_to_f32(xb)
+    n_floor = 0
+    for t in range(T):
+        a = Fraction(float(np.abs(x[t]).max()))
+        n_floor += a < _FLOOR
+        ac = max(a, _FLOOR)
+        assert _f32_bits(s[t, 0]) == _f32_bits(bf.f32_round(ac / 448)), t
+        inv = bf.f32_round(Fraction(448) / ac)
+        prod = (x[t].astype(np.float64) * inv).astype(np.float32)
+        np.testing.assert_array_equal(q[t], bf.e4m3_nearest(prod), err_msg="group %d" % t)
+    assert 10 < n_floor < T - 10
 
 
 def test_fp8_dispatch_rows_are_quantised_tokens():
