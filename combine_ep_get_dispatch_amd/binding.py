@@ -110,11 +110,17 @@ def _ptr(t: torch.Tensor | None):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _need(t: torch.Tensor, dtype, name: str, shape=None):
+def _is_gpu(t: torch.Tensor) -> bool:
+    return t.device.type == "cuda"
+
+
+def _need(t: torch.Tensor, dtype, name: str, shape=None, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if t.device.type != "cuda":
+    if not _is_gpu(t):
         raise ValueError("%s must be a GPU tensor" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if not t.is_contiguous():
@@ -136,7 +142,9 @@ def workspace_bytes(num_tokens: int, num_topk: int, num_experts: int, num_partit
 
 
 def new_workspace(num_tokens, num_topk, num_experts, num_partitions, device="cuda"):
-    """A zero-filled workspace for this shape (the header must start at zero)."""
+    """A workspace for this shape.  It needs no initialisation (every layout
+    call writes all that later calls read from it); it is zero-filled only so
+    that its contents are defined before the first call."""
     return torch.zeros(workspace_bytes(num_tokens, num_topk, num_experts, num_partitions),
                        dtype=torch.uint8, device=device)
 
@@ -158,12 +166,12 @@ def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_partitions
     if topk_idx.dim() != 2:
         raise ValueError("topk_idx must be [T, K]")
     T, K = topk_idx.shape
-    _need(topk_idx, torch.int64, "topk_idx")
     dev = topk_idx.device
+    _need(topk_idx, torch.int64, "topk_idx", device=dev)
     E, P = int(num_experts), int(num_partitions)
     if workspace is None:
         workspace = new_workspace(T, K, E, P, dev)
-    _need(workspace, torch.uint8, "workspace")
+    _need(workspace, torch.uint8, "workspace", device=dev)
     if out is None:
         out = Layout(torch.empty(E, dtype=torch.int32, device=dev),
                      torch.empty(P, dtype=torch.int32, device=dev),
@@ -172,6 +180,11 @@ def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_partitions
                      torch.empty(P + 1, dtype=torch.int32, device=dev), workspace)
     else:
         out.workspace = workspace
+    _need(out.num_tokens_per_expert, torch.int32, "num_tokens_per_expert", (E,), device=dev)
+    _need(out.num_tokens_per_partition, torch.int32, "num_tokens_per_partition", (P,), device=dev)
+    _need(out.is_token_in_partition, torch.uint8, "is_token_in_partition", (T, P), device=dev)
+    _need(out.expert_offsets, torch.int32, "expert_offsets", (E + 1,), device=dev)
+    _need(out.partition_offsets, torch.int32, "partition_offsets", (P + 1,), device=dev)
     _check(lib().ep_get_dispatch_layout(
         _ptr(topk_idx), T, K, E, P, _ptr(out.num_tokens_per_expert),
         _ptr(out.num_tokens_per_partition), _ptr(out.is_token_in_partition),
@@ -208,10 +221,10 @@ def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_part
         raise ValueError("x must be [T, H] and topk_idx [T, K]")
     T, H = x.shape
     K = topk_idx.shape[1]
-    _need(x, torch.bfloat16, "x")
-    _need(topk_idx, torch.int64, "topk_idx", (T, K))
-    _need(workspace, torch.uint8, "workspace")
     dev = x.device
+    _need(x, torch.bfloat16, "x", device=dev)
+    _need(topk_idx, torch.int64, "topk_idx", (T, K), device=dev)
+    _need(workspace, torch.uint8, "workspace", device=dev)
     R = T * K
     if out is None:
         out = Dispatched(
@@ -219,11 +232,11 @@ def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_part
             torch.empty((R, H // 128), dtype=torch.float32, device=dev) if fp8 else None,
             torch.empty(R, dtype=torch.int32, device=dev),
             torch.empty((T, K), dtype=torch.int32, device=dev))
-    _need(out.recv_x, torch.uint8 if fp8 else torch.bfloat16, "recv_x", (R, H))
+    _need(out.recv_x, torch.uint8 if fp8 else torch.bfloat16, "recv_x", (R, H), device=dev)
     if fp8:
-        _need(out.recv_scales, torch.float32, "recv_scales", (R, H // 128))
-    _need(out.recv_src_token, torch.int32, "recv_src_token", (R,))
-    _need(out.dst_row, torch.int32, "dst_row", (T, K))
+        _need(out.recv_scales, torch.float32, "recv_scales", (R, H // 128), device=dev)
+    _need(out.recv_src_token, torch.int32, "recv_src_token", (R,), device=dev)
+    _need(out.dst_row, torch.int32, "dst_row", (T, K), device=dev)
     _check(lib().ep_dispatch(
         _ptr(x), T, H, _ptr(topk_idx), K, int(num_experts), int(num_partitions),
         EP_DTYPE_FP8_E4M3 if fp8 else EP_DTYPE_BF16, _ptr(out.recv_x),
@@ -245,12 +258,12 @@ def layout_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int,
     T, H = x.shape
     K = topk_idx.shape[1]
     E, P = int(num_experts), int(num_partitions)
-    _need(x, torch.bfloat16, "x")
-    _need(topk_idx, torch.int64, "topk_idx", (T, K))
     dev = x.device
+    _need(x, torch.bfloat16, "x", device=dev)
+    _need(topk_idx, torch.int64, "topk_idx", (T, K), device=dev)
     if workspace is None:
         workspace = new_workspace(T, K, E, P, dev)
-    _need(workspace, torch.uint8, "workspace")
+    _need(workspace, torch.uint8, "workspace", device=dev)
     if out_layout is None:
         out_layout = Layout(torch.empty(E, dtype=torch.int32, device=dev),
                             torch.empty(P, dtype=torch.int32, device=dev),
@@ -267,16 +280,16 @@ def layout_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int,
             torch.empty(R, dtype=torch.int32, device=dev),
             torch.empty((T, K), dtype=torch.int32, device=dev))
     lo = out_layout
-    _need(lo.num_tokens_per_expert, torch.int32, "num_tokens_per_expert", (E,))
-    _need(lo.num_tokens_per_partition, torch.int32, "num_tokens_per_partition", (P,))
-    _need(lo.is_token_in_partition, torch.uint8, "is_token_in_partition", (T, P))
-    _need(lo.expert_offsets, torch.int32, "expert_offsets", (E + 1,))
-    _need(lo.partition_offsets, torch.int32, "partition_offsets", (P + 1,))
-    _need(out.recv_x, torch.uint8 if fp8 else torch.bfloat16, "recv_x", (R, H))
+    _need(lo.num_tokens_per_expert, torch.int32, "num_tokens_per_expert", (E,), device=dev)
+    _need(lo.num_tokens_per_partition, torch.int32, "num_tokens_per_partition", (P,), device=dev)
+    _need(lo.is_token_in_partition, torch.uint8, "is_token_in_partition", (T, P), device=dev)
+    _need(lo.expert_offsets, torch.int32, "expert_offsets", (E + 1,), device=dev)
+    _need(lo.partition_offsets, torch.int32, "partition_offsets", (P + 1,), device=dev)
+    _need(out.recv_x, torch.uint8 if fp8 else torch.bfloat16, "recv_x", (R, H), device=dev)
     if fp8:
-        _need(out.recv_scales, torch.float32, "recv_scales", (R, H // 128))
-    _need(out.recv_src_token, torch.int32, "recv_src_token", (R,))
-    _need(out.dst_row, torch.int32, "dst_row", (T, K))
+        _need(out.recv_scales, torch.float32, "recv_scales", (R, H // 128), device=dev)
+    _need(out.recv_src_token, torch.int32, "recv_src_token", (R,), device=dev)
+    _need(out.dst_row, torch.int32, "dst_row", (T, K), device=dev)
     _check(lib().ep_layout_dispatch_cu(
         _ptr(x), T, H, _ptr(topk_idx), K, E, P, EP_DTYPE_FP8_E4M3 if fp8 else EP_DTYPE_BF16,
         _ptr(lo.num_tokens_per_expert), _ptr(lo.num_tokens_per_partition),
@@ -305,15 +318,15 @@ def layout_dispatch_aligned(x: torch.Tensor, topk_idx: torch.Tensor, num_experts
     T, H = x.shape
     K = topk_idx.shape[1]
     E, P, A = int(num_experts), int(num_partitions), int(expert_alignment)
-    _need(x, torch.bfloat16, "x")
-    _need(topk_idx, torch.int64, "topk_idx", (T, K))
+    dev = x.device
+    _need(x, torch.bfloat16, "x", device=dev)
+    _need(topk_idx, torch.int64, "topk_idx", (T, K), device=dev)
     R = aligned_rows(T, K, E, A)
     if R == 0 and T > 0:
         raise ValueError("expert_alignment %d rejected for T=%d K=%d E=%d" % (A, T, K, E))
-    dev = x.device
     if workspace is None:
         workspace = new_workspace(T, K, E, P, dev)
-    _need(workspace, torch.uint8, "workspace")
+    _need(workspace, torch.uint8, "workspace", device=dev)
     if out_layout is None:
         out_layout = Layout(torch.empty(E, dtype=torch.int32, device=dev),
                             torch.empty(P, dtype=torch.int32, device=dev),
@@ -329,16 +342,16 @@ def layout_dispatch_aligned(x: torch.Tensor, topk_idx: torch.Tensor, num_experts
             torch.empty(R, dtype=torch.int32, device=dev),
             torch.empty((T, K), dtype=torch.int32, device=dev))
     lo = out_layout
-    _need(lo.num_tokens_per_expert, torch.int32, "num_tokens_per_expert", (E,))
-    _need(lo.num_tokens_per_partition, torch.int32, "num_tokens_per_partition", (P,))
-    _need(lo.is_token_in_partition, torch.uint8, "is_token_in_partition", (T, P))
-    _need(lo.expert_offsets, torch.int32, "expert_offsets", (E + 1,))
-    _need(lo.partition_offsets, torch.int32, "partition_offsets", (P + 1,))
-    _need(out.recv_x, torch.uint8 if fp8 else torch.bfloat16, "recv_x", (R, H))
+    _need(lo.num_tokens_per_expert, torch.int32, "num_tokens_per_expert", (E,), device=dev)
+    _need(lo.num_tokens_per_partition, torch.int32, "num_tokens_per_partition", (P,), device=dev)
+    _need(lo.is_token_in_partition, torch.uint8, "is_token_in_partition", (T, P), device=dev)
+    _need(lo.expert_offsets, torch.int32, "expert_offsets", (E + 1,), device=dev)
+    _need(lo.partition_offsets, torch.int32, "partition_offsets", (P + 1,), device=dev)
+    _need(out.recv_x, torch.uint8 if fp8 else torch.bfloat16, "recv_x", (R, H), device=dev)
     if fp8:
-        _need(out.recv_scales, torch.float32, "recv_scales", (R, H // 128))
-    _need(out.recv_src_token, torch.int32, "recv_src_token", (R,))
-    _need(out.dst_row, torch.int32, "dst_row", (T, K))
+        _need(out.recv_scales, torch.float32, "recv_scales", (R, H // 128), device=dev)
+    _need(out.recv_src_token, torch.int32, "recv_src_token", (R,), device=dev)
+    _need(out.dst_row, torch.int32, "dst_row", (T, K), device=dev)
     _check(lib().ep_layout_dispatch_aligned(
         _ptr(x), T, H, _ptr(topk_idx), K, E, P, A, EP_DTYPE_FP8_E4M3 if fp8 else EP_DTYPE_BF16,
         _ptr(lo.num_tokens_per_expert), _ptr(lo.num_tokens_per_partition),
@@ -373,12 +386,12 @@ def dispatch_dedup(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int,
     E, P = int(num_experts), int(num_partitions)
     Kp = min(K, P)
     RD = T * Kp
-    _need(x, torch.bfloat16, "x")
-    _need(topk_idx, torch.int64, "topk_idx", (T, K))
     dev = x.device
+    _need(x, torch.bfloat16, "x", device=dev)
+    _need(topk_idx, torch.int64, "topk_idx", (T, K), device=dev)
     if workspace is None:
         workspace = new_workspace(T, K, E, P, dev)
-    _need(workspace, torch.uint8, "workspace")
+    _need(workspace, torch.uint8, "workspace", device=dev)
     if out_layout is None:
         out_layout = Layout(torch.empty(E, dtype=torch.int32, device=dev),
                             torch.empty(P, dtype=torch.int32, device=dev),
@@ -397,19 +410,19 @@ def dispatch_dedup(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int,
             torch.empty(T * K, dtype=torch.int32, device=dev),
             torch.empty((T, K), dtype=torch.int32, device=dev))
     lo = out_layout
-    _need(lo.num_tokens_per_expert, torch.int32, "num_tokens_per_expert", (E,))
-    _need(lo.num_tokens_per_partition, torch.int32, "num_tokens_per_partition", (P,))
-    _need(lo.is_token_in_partition, torch.uint8, "is_token_in_partition", (T, P))
-    _need(lo.expert_offsets, torch.int32, "expert_offsets", (E + 1,))
-    _need(lo.partition_offsets, torch.int32, "partition_offsets", (P + 1,))
-    _need(out.partition_token_offsets, torch.int32, "partition_token_offsets", (P + 1,))
-    _need(out.recv_x, torch.uint8 if fp8 else torch.bfloat16, "recv_x", (RD, H))
+    _need(lo.num_tokens_per_expert, torch.int32, "num_tokens_per_expert", (E,), device=dev)
+    _need(lo.num_tokens_per_partition, torch.int32, "num_tokens_per_partition", (P,), device=dev)
+    _need(lo.is_token_in_partition, torch.uint8, "is_token_in_partition", (T, P), device=dev)
+    _need(lo.expert_offsets, torch.int32, "expert_offsets", (E + 1,), device=dev)
+    _need(lo.partition_offsets, torch.int32, "partition_offsets", (P + 1,), device=dev)
+    _need(out.partition_token_offsets, torch.int32, "partition_token_offsets", (P + 1,), device=dev)
+    _need(out.recv_x, torch.uint8 if fp8 else torch.bfloat16, "recv_x", (RD, H), device=dev)
     if fp8:
-        _need(out.recv_scales, torch.float32, "recv_scales", (RD, H // 128))
-    _need(out.recv_src_token, torch.int32, "recv_src_token", (RD,))
-    _need(out.recv_topk_idx, torch.int32, "recv_topk_idx", (RD, K))
-    _need(out.slot_src_row, torch.int32, "slot_src_row", (T * K,))
-    _need(out.dst_row, torch.int32, "dst_row", (T, K))
+        _need(out.recv_scales, torch.float32, "recv_scales", (RD, H // 128), device=dev)
+    _need(out.recv_src_token, torch.int32, "recv_src_token", (RD,), device=dev)
+    _need(out.recv_topk_idx, torch.int32, "recv_topk_idx", (RD, K), device=dev)
+    _need(out.slot_src_row, torch.int32, "slot_src_row", (T * K,), device=dev)
+    _need(out.dst_row, torch.int32, "dst_row", (T, K), device=dev)
     _check(lib().ep_dispatch_dedup(
         _ptr(x), T, H, _ptr(topk_idx), K, E, P, EP_DTYPE_FP8_E4M3 if fp8 else EP_DTYPE_BF16,
         _ptr(lo.num_tokens_per_expert), _ptr(lo.num_tokens_per_partition),
@@ -441,9 +454,9 @@ def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: i
     T, H = x.shape
     K = topk_idx.shape[1]
     E, C = int(num_experts), int(capacity)
-    _need(x, torch.bfloat16, "x")
-    _need(topk_idx, torch.int64, "topk_idx", (T, K))
     dev = x.device
+    _need(x, torch.bfloat16, "x", device=dev)
+    _need(topk_idx, torch.int64, "topk_idx", (T, K), device=dev)
     R = E * C
     if out is None:
         out = LowLatencyDispatched(
@@ -453,13 +466,13 @@ def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: i
             torch.empty(R, dtype=torch.int32, device=dev),
             torch.empty((T, K), dtype=torch.int32, device=dev),
             torch.empty(1, dtype=torch.int64, device=dev))
-    _need(out.num_tokens_per_expert, torch.int32, "num_tokens_per_expert", (E,))
-    _need(out.recv_x, torch.uint8 if fp8 else torch.bfloat16, "recv_x", (R, H))
+    _need(out.num_tokens_per_expert, torch.int32, "num_tokens_per_expert", (E,), device=dev)
+    _need(out.recv_x, torch.uint8 if fp8 else torch.bfloat16, "recv_x", (R, H), device=dev)
     if fp8:
-        _need(out.recv_scales, torch.float32, "recv_scales", (R, H // 128))
-    _need(out.recv_src_token, torch.int32, "recv_src_token", (R,))
-    _need(out.dst_row, torch.int32, "dst_row", (T, K))
-    _need(out.num_invalid, torch.int64, "num_invalid", (1,))
+        _need(out.recv_scales, torch.float32, "recv_scales", (R, H // 128), device=dev)
+    _need(out.recv_src_token, torch.int32, "recv_src_token", (R,), device=dev)
+    _need(out.dst_row, torch.int32, "dst_row", (T, K), device=dev)
+    _need(out.num_invalid, torch.int64, "num_invalid", (1,), device=dev)
     _check(lib().ep_low_latency_dispatch(
         _ptr(x), T, H, _ptr(topk_idx), K, E, C, EP_DTYPE_FP8_E4M3 if fp8 else EP_DTYPE_BF16,
         _ptr(out.num_tokens_per_expert), _ptr(out.recv_x),
@@ -476,12 +489,13 @@ def combine(y: torch.Tensor, dst_row: torch.Tensor, topk_weights: torch.Tensor,
         raise ValueError("y must be [R, H] and dst_row [T, K]")
     T, K = dst_row.shape
     H = y.shape[1]
-    _need(y, torch.bfloat16, "y")
-    _need(dst_row, torch.int32, "dst_row")
-    _need(topk_weights, torch.float32, "topk_weights", (T, K))
+    dev = y.device
+    _need(y, torch.bfloat16, "y", device=dev)
+    _need(dst_row, torch.int32, "dst_row", device=dev)
+    _need(topk_weights, torch.float32, "topk_weights", (T, K), device=dev)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
-    _need(out, torch.bfloat16, "out", (T, H))
+    _need(out, torch.bfloat16, "out", (T, H), device=dev)
     _check(lib().ep_combine_cu(_ptr(y), y.shape[0], _ptr(dst_row), _ptr(topk_weights), T, K, H,
                                _ptr(out), int(num_cus), _stream(y)), "ep_combine_cu")
     return out

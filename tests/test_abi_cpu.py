@@ -282,3 +282,43 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises((ValueError, TypeError)):
         b.combine(torch.zeros((8, 16), dtype=torch.bfloat16),
                   torch.zeros((4, 2), dtype=torch.int32), torch.zeros((4, 2)))
+
+
+class _NoLaunch:
+    """Stands in for the library: any call into it fails the test."""
+    def __getattr__(self, name):
+        raise AssertionError("the binding called %s before rejecting its arguments" % name)
+
+
+@pytest.mark.parametrize("field,bad", [
+    ("num_tokens_per_expert", lambda E, P, T: torch.zeros(E - 1, dtype=torch.int32)),
+    ("num_tokens_per_partition", lambda E, P, T: torch.zeros(P, dtype=torch.int64)),
+    ("is_token_in_partition", lambda E, P, T: torch.zeros((T + 1, P), dtype=torch.uint8)),
+    ("expert_offsets", lambda E, P, T: torch.zeros(E, dtype=torch.int32)),
+    ("partition_offsets", lambda E, P, T: torch.zeros(2 * (P + 1), dtype=torch.int32)[::2]),
+])
+def test_get_dispatch_layout_checks_a_caller_layout(monkeypatch, field, bad):
+    """A Layout passed in as ``out`` (for instance one built for another T or
+    P) is checked before anything is launched: the C ABI cannot see buffer
+    sizes, so a wrong one would let the layout kernels write past it."""
+    monkeypatch.setattr(b, "_is_gpu", lambda t: True)     # CPU tensors stand in for GPU ones
+    monkeypatch.setattr(b, "lib", lambda: _NoLaunch())
+    T, K, E, P = 6, 2, 8, 4
+    idx = torch.zeros((T, K), dtype=torch.int64)
+    ws = torch.zeros(4096, dtype=torch.uint8)
+    lay = b.Layout(torch.zeros(E, dtype=torch.int32), torch.zeros(P, dtype=torch.int32),
+                   torch.zeros((T, P), dtype=torch.uint8), torch.zeros(E + 1, dtype=torch.int32),
+                   torch.zeros(P + 1, dtype=torch.int32), ws)
+    setattr(lay, field, bad(E, P, T))
+    with pytest.raises((ValueError, TypeError)):
+        b.get_dispatch_layout(idx, E, P, workspace=ws, out=lay)
+
+
+def test_binding_rejects_tensors_on_another_device(monkeypatch):
+    """Every tensor of a call must be on the device of its first input."""
+    monkeypatch.setattr(b, "_is_gpu", lambda t: True)
+    monkeypatch.setattr(b, "lib", lambda: _NoLaunch())
+    x = torch.zeros((4, 16), dtype=torch.bfloat16)
+    idx = torch.zeros((4, 2), dtype=torch.int64, device="meta")
+    with pytest.raises(ValueError, match="must be on"):
+        b.dispatch(x, idx, 4, 2, torch.zeros(4096, dtype=torch.uint8))
