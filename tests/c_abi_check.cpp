@@ -1,7 +1,11 @@
 // A C++ caller of the C ABI alone (include/ep.h, hipMalloc, no torch): one
-// offsets-layout step in bf16 and in FP8, then combine, with structural checks
-// that need no reference implementation:
-//   counts sum to the valid slots, offsets are their exclusive prefix, every
+// offsets-layout step in bf16 and in FP8, each both as the two calls
+// ep_get_dispatch_layout -> ep_dispatch and as the one call ep_layout_dispatch,
+// then ep_combine and ep_get_device_error, with checks that need no reference
+// implementation:
+//   the expert counts equal a count taken on the host, the one invalid id is
+//   reported and its slot gets no row, counts sum to the valid slots, offsets
+//   are their exclusive prefix, every
 //   valid slot gets a distinct row inside its expert's run, rows inside a run
 //   are in token order, recv_src_token inverts dst_row, bf16 rows are bitwise
 //   copies of their tokens, every FP8 group's largest element encodes to +-448
@@ -15,6 +19,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <utility>
 #include <vector>
 
 #include "ep.h"
@@ -65,11 +70,20 @@ int main() {
     const int32_t T = 512, H = 1024, E = 64, P = 8, K = 6, Ep = E / P, G = H / 128;
     const int32_t R = T * K;
 
-    // Routing: six distinct experts per token, slot 5 masked on every 17th token.
+    // Routing: six distinct experts per token, slot 5 masked on every 17th token,
+    // and one invalid id (slot 4 of token 3).
     std::vector<int64_t> idx((size_t)T * K);
     for (int t = 0; t < T; ++t)
         for (int k = 0; k < K; ++k)
             idx[(size_t)t * K + k] = (k == 5 && t % 17 == 0) ? -1 : (t * 5 + k * 11) % E;
+    idx[(size_t)3 * K + 4] = E + 5;
+    std::vector<int> host_cnt(E, 0);
+    int valid = 0;
+    for (int64_t v : idx)
+        if (v >= 0 && v < E) {
+            ++host_cnt[v];
+            ++valid;
+        }
     // Tokens: bf16 values with a per-(token, group) range, exact small multiples of 1/8.
     std::vector<uint16_t> x((size_t)T * H);
     for (int t = 0; t < T; ++t)
@@ -122,17 +136,32 @@ int main() {
                               d_ws, 16, stream) == EP_ERR_WORKSPACE,
            "small workspace accepted");
 
-    for (int fp8 = 0; fp8 < 2; ++fp8) {
+    for (int run = 0; run < 4; ++run) {
+        const int fp8 = run & 1, two_calls = run >> 1;
         void* rx = fp8 ? d_rx8 : d_rx16;
-        EP_OK_CALL(ep_layout_dispatch(d_x, T, H, (const int64_t*)d_idx, K, E, P,
-                                      fp8 ? EP_DTYPE_FP8_E4M3 : EP_DTYPE_BF16, d_cnt_e, d_cnt_p,
-                                      d_inp, d_off_e, d_off_p, rx, fp8 ? (float*)d_rs : nullptr,
-                                      d_src, d_dst, d_ws, ws_bytes, stream));
+        const ep_dtype_t dt = fp8 ? EP_DTYPE_FP8_E4M3 : EP_DTYPE_BF16;
+        // clear the outputs, so that every value checked below comes from this run
+        const std::pair<void*, size_t> outs[] = {{d_cnt_e, E * 4}, {d_cnt_p, P * 4},
+                                                 {d_off_e, (E + 1) * 4}, {d_off_p, (P + 1) * 4},
+                                                 {d_src, R * 4}, {d_dst, R * 4}};
+        for (const auto& o : outs) HIP_OK(hipMemset(o.first, 0x7f, o.second));
+        if (two_calls) {
+            EP_OK_CALL(ep_get_dispatch_layout((const int64_t*)d_idx, T, K, E, P, d_cnt_e, d_cnt_p,
+                                              d_inp, d_off_e, d_off_p, d_ws, ws_bytes, stream));
+            EP_OK_CALL(ep_dispatch(d_x, T, H, (const int64_t*)d_idx, K, E, P, dt, rx,
+                                   fp8 ? (float*)d_rs : nullptr, d_src, d_dst, d_ws, ws_bytes,
+                                   stream));
+        } else {
+            EP_OK_CALL(ep_layout_dispatch(d_x, T, H, (const int64_t*)d_idx, K, E, P, dt, d_cnt_e,
+                                          d_cnt_p, d_inp, d_off_e, d_off_p, rx,
+                                          fp8 ? (float*)d_rs : nullptr, d_src, d_dst, d_ws,
+                                          ws_bytes, stream));
+        }
         if (!fp8)   // identity experts: y = the bf16 receive rows
             EP_OK_CALL(ep_combine(d_rx16, R, d_dst, (const float*)d_w, T, K, H, d_out, stream));
         int64_t ninv = -1;
         EP_OK_CALL(ep_get_device_error(d_ws, ws_bytes, &ninv, stream));   // synchronises
-        expect(ninv == 0, "invalid ids reported");
+        expect(ninv == 1, "the one invalid id is not reported");
 
         std::vector<int32_t> cnt_e(E), cnt_p(P), off_e(E + 1), off_p(P + 1), src(R), dst(R);
         std::vector<uint8_t> inp((size_t)T * P);
@@ -144,10 +173,9 @@ int main() {
         HIP_OK(hipMemcpy(dst.data(), d_dst, R * 4, hipMemcpyDeviceToHost));
         HIP_OK(hipMemcpy(inp.data(), d_inp, (size_t)T * P, hipMemcpyDeviceToHost));
 
-        int valid = 0;
-        for (int64_t v : idx) valid += v >= 0;
         int sum = 0;
         for (int e = 0; e < E; ++e) {
+            expect(cnt_e[e] == host_cnt[e], "expert count differs from the host's count");
             expect(off_e[e] == sum, "expert offsets are not the prefix of the counts");
             sum += cnt_e[e];
         }
@@ -164,8 +192,8 @@ int main() {
             for (int k = 0; k < K; ++k) {
                 const int64_t e = idx[(size_t)t * K + k];
                 const int r = dst[(size_t)t * K + k];
-                if (e < 0) {
-                    expect(r == -1, "masked slot got a row");
+                if (e < 0 || e >= E) {
+                    expect(r == -1, "masked or invalid slot got a row");
                     continue;
                 }
                 expect(r >= off_e[e] && r < off_e[e + 1], "row outside its expert's run");

@@ -1,6 +1,8 @@
 """The C ABI used from C++ alone (GPU): tests/c_abi_check.cpp allocates with
-hipMalloc, calls ep_layout_dispatch (bf16 and FP8) and ep_combine, and checks
-the results' structure (counts and offsets, distinct in-run rows in token
+hipMalloc, calls ep_get_dispatch_layout -> ep_dispatch and, separately,
+ep_layout_dispatch (bf16 and FP8 each), then ep_combine and
+ep_get_device_error, and checks the results (expert counts against a count on
+the host, the one invalid id reported, offsets, distinct in-run rows in token
 order, recv_src_token inverting dst_row, bf16 rows as token copies, FP8 group
 maxima at 448 with scale max|x|/448, combine of identity experts returning x)
 and that bad arguments are refused.  It runs as a child process."""
