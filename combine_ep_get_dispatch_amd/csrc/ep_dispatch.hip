@@ -228,7 +228,7 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void dispatch_kernel(
     const uint16_t* __restrict__ x, int T, int H, int K, const WsHeader* __restrict__ hdr,
     const int* __restrict__ rows, void* __restrict__ recv_x, float* __restrict__ recv_scales,
     int32_t* __restrict__ recv_src, int32_t* __restrict__ dst_row, int nchunk, int nrows) {
-    extern __shared__ float s_scale[];   // [G] scales of this token (FP8)
+    extern __shared__ EP_LDS_ALIGN float s_scale[];   // [G] scales of this token (FP8)
     if constexpr (!LOOP) {
         dispatch_token<FP8>(blockIdx.x, x, H, K, hdr, rows, recv_x, recv_scales, recv_src,
                             dst_row, nchunk, nrows, s_scale);
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void layout_dispatch_kernel(
     int32_t* __restrict__ off_e, int32_t* __restrict__ off_p, void* __restrict__ recv_x,
     float* __restrict__ recv_scales, int32_t* __restrict__ recv_src,
     int32_t* __restrict__ dst_row, int nchunk, int nrows, int gsize_loop) {
-    extern __shared__ float s_scale[];   // [groups][G] scales of the group's token (FP8)
+    extern __shared__ EP_LDS_ALIGN float s_scale[];   // [groups][G] scales of the group's token (FP8)
     __shared__ int s_row[kBudgetGroups][64];   // receive row of slot k (K <= 64)
     __shared__ int s_n[kBudgetGroups];         // N
     if constexpr (!LOOP) {
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void dedup_dispatch_kernel(
     float* __restrict__ recv_scales, int32_t* __restrict__ recv_src,
     int32_t* __restrict__ recv_topk_idx, int32_t* __restrict__ slot_src,
     int32_t* __restrict__ dst_row, int nchunk, int nrows, int ndrows) {
-    extern __shared__ float s_scale[];   // [G] scales of this token (FP8)
+    extern __shared__ EP_LDS_ALIGN float s_scale[];   // [G] scales of this token (FP8)
     __shared__ int s_pk[64];             // packed slot k (K <= 64)
     __shared__ int s_erow[64];           // expert-major row of slot k
     __shared__ int s_drow[64];           // de-duplicated row of slot k's partition
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void ll_dispatch_kernel(
     int C, int32_t* __restrict__ cnt_e, void* __restrict__ recv_x,
     float* __restrict__ recv_scales, int32_t* __restrict__ recv_src,
     int32_t* __restrict__ dst_row, int64_t* __restrict__ num_invalid, int nchunk) {
-    extern __shared__ int smem[];
+    extern __shared__ EP_LDS_ALIGN int smem[];
     int* h_pre = smem;                                      // [E] slots of tokens < t
     int* h_all = smem + E;                                  // [E] all valid slots
     float* s_scale = reinterpret_cast<float*>(smem + 2 * E); // [G] (FP8)

@@ -8,6 +8,14 @@
 
 namespace ep {
 
+// Alignment of every dynamic-LDS array (extern __shared__).  The dynamic area
+// follows a kernel's static LDS, which may end at any 4-byte boundary; the
+// attribute makes the compiler pad the static part so that the dynamic base
+// is 16-byte aligned.  Views carved out of a dynamic array may then use LDS
+// accesses up to 16 bytes wide, provided their offsets are multiples of their
+// access width; an 8- or 16-byte access to a less aligned LDS address faults.
+#define EP_LDS_ALIGN __attribute__((aligned(16)))
+
 // CU budget: the *_cu entry points launch at most num_cus workgroups of this
 // size (or the kernel's own size) that loop over their work, so that the
 // hardware places them on at most num_cus CUs.

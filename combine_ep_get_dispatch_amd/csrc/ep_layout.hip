@@ -119,8 +119,8 @@ __device__ int block_exclusive_scan(int* a, int n, int* red) {
 // table: every lane ORs its bit into mtab[e] (lanes 0-31 the first word,
 // 32-63 the second), reads both words back and clears them -- one wave's LDS
 // operations complete in issue order, so the reads see the whole chunk's
-// bits and the clears follow every read.  (32-bit words, so that only 4-byte
-// alignment is needed: the dynamic LDS need not start 8-byte aligned.)  The
+// bits and the clears follow every read.  (32-bit words: the tables start at
+// an offset of the dynamic area that is only a multiple of 4 bytes.)  The
 // table costs a few LDS operations per chunk instead of the ballots' VALU
 // work, which is what bounds this loop on the few workgroups a layout uses.
 //
@@ -163,15 +163,24 @@ __device__ void rank_entries(const Id* ids, int n, int E, int ebits, int* wcnt, 
         uint64_t m;
         if (myt) {
             unsigned* w = myt + 2 * e;
+            // The three phases touch different words of the table (a lane ORs
+            // one word, reads two), so nothing but these compiler fences keeps
+            // their LDS operations in the order written; the hardware then
+            // completes one wave's LDS operations in issue order.
             if (valid) __hip_atomic_fetch_or(w + (lane >> 5), 1u << (lane & 31), __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_WAVEFRONT);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
             unsigned lo = 0, hi = 0;
             if (valid) {
                 lo = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
                 hi = __hip_atomic_load(w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+            }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (valid) {
                 __hip_atomic_store(w, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
                 __hip_atomic_store(w + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
             }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the next chunk's ORs follow the clears
             m = ((uint64_t)hi << 32) | lo;
         } else {
             m = __ballot(valid);
@@ -475,7 +484,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_fused_kernel(
     int TB, int ebits, int* __restrict__ rows, uint8_t* __restrict__ in_part, int vec_rows,
     WsHeader* __restrict__ hdr, int32_t* __restrict__ cnt_e, int32_t* __restrict__ cnt_p,
     int32_t* __restrict__ off_e, int32_t* __restrict__ off_p) {
-    extern __shared__ int smem[];
+    extern __shared__ EP_LDS_ALIGN int smem[];
     int* bef = smem;                               // [E] slots of e before this block's
     int* aft = bef + E;                            // [E] ... after this block's
     int* own = aft + E;                            // [E] ... in this block
@@ -573,7 +582,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
     int* __restrict__ rows, uint8_t* __restrict__ in_part, int vec_rows,
     int* __restrict__ pre, int* __restrict__ prank, int* __restrict__ ppre) {
     constexpr bool PRE = MODE != kCountPlain;
-    extern __shared__ int smem[];
+    extern __shared__ EP_LDS_ALIGN int smem[];
     int* wcnt = smem;                              // [waves][E]
     int* ids = wcnt + kLayoutWaves * E;            // [kLayoutEntries] stored ids
     int* rnk = ids + kLayoutEntries;               // [kLayoutEntries]
@@ -714,7 +723,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finalize_kernel(
     WsHeader* __restrict__ hdr, int32_t* __restrict__ cnt_e, int32_t* __restrict__ cnt_p,
     int32_t* __restrict__ off_e, int32_t* __restrict__ off_p, int align,
     int32_t* __restrict__ recv_src, int64_t R) {
-    extern __shared__ int smem[];
+    extern __shared__ EP_LDS_ALIGN int smem[];
     int* off = smem;          // [E] totals, then exclusive offsets
     int* bef = off + E;       // [E] rows of e in blocks before this one
     int* tot = bef + E;       // [E] totals (kept for the outputs)

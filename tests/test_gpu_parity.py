@@ -16,7 +16,7 @@ import torch
 
 from combine_ep_get_dispatch_amd import binding as ep
 from combine_ep_get_dispatch_amd import workloads as wl
-from parity import announce, check_case, run_gpu
+from parity import announce, check_case, run_gpu, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -137,13 +137,53 @@ def test_workspace_reuse_across_shapes():
         compare(g, run_oracle(case), case)
 
 
-def test_deterministic_across_runs():
-    case = wl.make("decode")
-    announce("determinism decode")
-    a = run_gpu(case)
-    b = run_gpu(case)
+def _step_outputs(case, fill):
+    """The benchmark's step (ep_layout_dispatch -> ep_combine) on cuda:0 into
+    outputs pre-filled with the byte ``fill``; returns the outputs (on the GPU)."""
+    idx = torch.from_numpy(case.topk_idx).cuda()
+    x = to_dev_bf16(case.x_bits)
+    y = to_dev_bf16(case.y_bits)
+    w = torch.from_numpy(case.topk_weights).cuda()
+    T, H, E, P, K, R = case.T, case.H, case.E, case.P, case.K, case.T * case.K
+
+    def filled(shape, dtype):
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        return torch.full((n,), fill, dtype=torch.uint8, device="cuda").view(dtype).view(shape)
+    ws = filled((ep.workspace_bytes(T, K, E, P),), torch.uint8)
+    lay = ep.Layout(filled((E,), torch.int32), filled((P,), torch.int32),
+                    filled((T, P), torch.uint8), filled((E + 1,), torch.int32),
+                    filled((P + 1,), torch.int32), ws)
+    d = ep.Dispatched(filled((R, H), torch.uint8 if case.fp8 else torch.bfloat16),
+                      filled((R, H // 128), torch.float32) if case.fp8 else None,
+                      filled((R,), torch.int32), filled((T, K), torch.int32))
+    out = filled((T, H), torch.bfloat16)
+    ep.layout_dispatch(x, idx, E, P, workspace=ws, fp8=case.fp8, out_layout=lay, out=d)
+    ep.combine(y, d.dst_row, w, out=out)
+    torch.cuda.synchronize()
+    res = {f: getattr(lay, f) for f in ("num_tokens_per_expert", "num_tokens_per_partition",
+                                        "is_token_in_partition", "expert_offsets",
+                                        "partition_offsets")}
+    res.update(recv_x=d.recv_x, recv_src_token=d.recv_src_token, dst_row=d.dst_row, out=out)
+    if case.fp8:
+        res["recv_scales"] = d.recv_scales
+    return res
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skewed", "coarse"])
+def test_deterministic_across_runs_full_size(name):
+    """Run the benchmark's step twice on the same inputs at the configuration's
+    full size, each time into outputs pre-filled with a different byte, and
+    compare every output bitwise: nothing depends on scheduling order, and
+    nothing is left over from the first run."""
+    case = wl.make(name)
+    announce("determinism %s" % name)
+    a = _step_outputs(case, 0xA5)
+    b = _step_outputs(case, 0x5A)
     for k in a:
-        np.testing.assert_array_equal(np.asarray(a[k]), np.asarray(b[k]), err_msg=k)
+        ua = a[k].contiguous().view(torch.uint8)
+        ub = b[k].contiguous().view(torch.uint8)
+        assert torch.equal(ua, ub), "%s differs between two runs of %s" % (k, name)
+        assert ua.numel() == 0 or not bool((ua == 0xA5).all()), k   # the run wrote it
 
 
 def test_rows_past_the_valid_ones_are_untouched():
