@@ -53,6 +53,9 @@ SIGNATURES = {
     "ep_layout_dispatch": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _i32, ctypes.c_int,
                                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                           _vp]),
+    "ep_layout_dispatch_static": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _i32,
+                                                 ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                 _vp, _vp, _vp]),
     "ep_aligned_rows": (_i64, [_i32, _i32, _i32, _i32]),
     "ep_layout_dispatch_aligned": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _i32, _i32,
                                                   ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -297,6 +300,55 @@ def layout_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int,
         _ptr(out.recv_x), _ptr(out.recv_scales) if fp8 else None, _ptr(out.recv_src_token),
         _ptr(out.dst_row), _ptr(workspace), workspace.numel(), int(num_cus), _stream(x)),
         "ep_layout_dispatch_cu")
+    return out_layout, out
+
+
+def layout_dispatch_static(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int,
+                           num_partitions: int, fp8: bool = False,
+                           out_layout: Layout | None = None, out: Dispatched | None = None):
+    """ep_layout_dispatch_static: the outputs of layout_dispatch, with the
+    library's static per-GPU scratch as the workspace (the C call allocates
+    nothing; outputs not given are allocated here).  The Layout's workspace
+    is None: the invalid-id count is not reported.  Returns (Layout,
+    Dispatched)."""
+    if x.dim() != 2 or topk_idx.dim() != 2:
+        raise ValueError("x must be [T, H] and topk_idx [T, K]")
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    E, P = int(num_experts), int(num_partitions)
+    dev = x.device
+    _need(x, torch.bfloat16, "x", device=dev)
+    _need(topk_idx, torch.int64, "topk_idx", (T, K), device=dev)
+    if out_layout is None:
+        out_layout = Layout(torch.empty(E, dtype=torch.int32, device=dev),
+                            torch.empty(P, dtype=torch.int32, device=dev),
+                            torch.empty((T, P), dtype=torch.uint8, device=dev),
+                            torch.empty(E + 1, dtype=torch.int32, device=dev),
+                            torch.empty(P + 1, dtype=torch.int32, device=dev), None)
+    R = T * K
+    if out is None:
+        out = Dispatched(
+            torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev),
+            torch.empty((R, H // 128), dtype=torch.float32, device=dev) if fp8 else None,
+            torch.empty(R, dtype=torch.int32, device=dev),
+            torch.empty((T, K), dtype=torch.int32, device=dev))
+    lo = out_layout
+    _need(lo.num_tokens_per_expert, torch.int32, "num_tokens_per_expert", (E,), device=dev)
+    _need(lo.num_tokens_per_partition, torch.int32, "num_tokens_per_partition", (P,), device=dev)
+    _need(lo.is_token_in_partition, torch.uint8, "is_token_in_partition", (T, P), device=dev)
+    _need(lo.expert_offsets, torch.int32, "expert_offsets", (E + 1,), device=dev)
+    _need(lo.partition_offsets, torch.int32, "partition_offsets", (P + 1,), device=dev)
+    _need(out.recv_x, torch.uint8 if fp8 else torch.bfloat16, "recv_x", (R, H), device=dev)
+    if fp8:
+        _need(out.recv_scales, torch.float32, "recv_scales", (R, H // 128), device=dev)
+    _need(out.recv_src_token, torch.int32, "recv_src_token", (R,), device=dev)
+    _need(out.dst_row, torch.int32, "dst_row", (T, K), device=dev)
+    _check(lib().ep_layout_dispatch_static(
+        _ptr(x), T, H, _ptr(topk_idx), K, E, P, EP_DTYPE_FP8_E4M3 if fp8 else EP_DTYPE_BF16,
+        _ptr(lo.num_tokens_per_expert), _ptr(lo.num_tokens_per_partition),
+        _ptr(lo.is_token_in_partition), _ptr(lo.expert_offsets), _ptr(lo.partition_offsets),
+        _ptr(out.recv_x), _ptr(out.recv_scales) if fp8 else None, _ptr(out.recv_src_token),
+        _ptr(out.dst_row), _stream(x)), "ep_layout_dispatch_static")
     return out_layout, out
 
 

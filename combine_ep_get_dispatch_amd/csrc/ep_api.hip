@@ -4,6 +4,16 @@
 #include "ep.h"
 #include "ep_internal.h"
 
+#include <atomic>
+#include <mutex>
+
+// Device scratch of ep_layout_dispatch_static: the workspace of callers that
+// cannot allocate.  Every GPU the library runs on holds its own copy until
+// the process ends.  In host code `scratch` names a host-side stand-in, not a
+// device address: only the pointer that hipGetSymbolAddress returns for the
+// current device may reach a kernel or a copy.
+static __device__ __align__(256) unsigned char scratch[EP_STATIC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int64_t kMaxRows = (int64_t)1 << 31;
@@ -20,6 +30,30 @@ ep_status_t check_routing_shape(int32_t T, int32_t K, int32_t E, int32_t P) {
 }
 
 ep_status_t from_hip(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
+
+// Address of the current device's copy of `scratch`, looked up once per
+// device (with that device current) and kept.
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kScratchDevices];
+std::mutex g_scratch_mu;
+
+ep_status_t device_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return EP_ERR_HIP;
+    if (dev < 0 || dev >= kScratchDevices) return EP_ERR_UNSUPPORTED;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+                return EP_ERR_HIP;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return EP_OK;
+}
 
 }  // namespace
 
@@ -78,6 +112,40 @@ ep_status_t ep_dispatch(const void* x, int32_t num_tokens, int32_t hidden,
                                         T * K, static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the one-call layout + dispatch (the workspace apart).
+ep_status_t check_layout_dispatch(const void* x, int32_t T, int32_t H, const int64_t* topk_idx,
+                                  int32_t K, int32_t E, int32_t P, ep_dtype_t out_dtype,
+                                  const int32_t* num_tokens_per_expert,
+                                  const int32_t* num_tokens_per_partition,
+                                  const uint8_t* is_token_in_partition,
+                                  const int32_t* expert_offsets, const int32_t* partition_offsets,
+                                  const void* recv_x, const float* recv_scales,
+                                  const int32_t* recv_src_token, const int32_t* dst_row) {
+    ep_status_t st = check_routing_shape(T, K, E, P);
+    if (st != EP_OK) return st;
+    if (out_dtype != EP_DTYPE_BF16 && out_dtype != EP_DTYPE_FP8_E4M3) return EP_ERR_INVALID_ARG;
+    const bool fp8 = out_dtype == EP_DTYPE_FP8_E4M3;
+    if (H <= 0 || H % 8 != 0 || (fp8 && H % 128 != 0)) return EP_ERR_INVALID_ARG;
+    if (!num_tokens_per_expert || !num_tokens_per_partition || !expert_offsets ||
+        !partition_offsets)
+        return EP_ERR_INVALID_ARG;
+    if (T > 0) {
+        if (!x || !topk_idx || !is_token_in_partition || !recv_x || !recv_src_token || !dst_row)
+            return EP_ERR_INVALID_ARG;
+        if (fp8 && !recv_scales) return EP_ERR_INVALID_ARG;
+        if (!aligned16(x) || !aligned16(recv_x)) return EP_ERR_INVALID_ARG;
+    }
+    return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 ep_status_t ep_layout_dispatch_cu(const void* x, int32_t num_tokens, int32_t hidden,
                                   const int64_t* topk_idx, int32_t num_topk, int32_t num_experts,
                                   int32_t num_partitions, ep_dtype_t out_dtype,
@@ -88,21 +156,14 @@ ep_status_t ep_layout_dispatch_cu(const void* x, int32_t num_tokens, int32_t hid
                                   int32_t* recv_src_token, int32_t* dst_row, void* workspace,
                                   size_t workspace_bytes, int32_t num_cus, void* stream) {
     const int32_t T = num_tokens, H = hidden, K = num_topk, E = num_experts, P = num_partitions;
-    ep_status_t st = check_routing_shape(T, K, E, P);
+    ep_status_t st = check_layout_dispatch(x, T, H, topk_idx, K, E, P, out_dtype,
+                                           num_tokens_per_expert, num_tokens_per_partition,
+                                           is_token_in_partition, expert_offsets,
+                                           partition_offsets, recv_x, recv_scales,
+                                           recv_src_token, dst_row);
     if (st != EP_OK) return st;
-    if (out_dtype != EP_DTYPE_BF16 && out_dtype != EP_DTYPE_FP8_E4M3) return EP_ERR_INVALID_ARG;
+    if (!workspace || num_cus < 0) return EP_ERR_INVALID_ARG;
     const bool fp8 = out_dtype == EP_DTYPE_FP8_E4M3;
-    if (H <= 0 || H % 8 != 0 || (fp8 && H % 128 != 0)) return EP_ERR_INVALID_ARG;
-    if (!num_tokens_per_expert || !num_tokens_per_partition || !expert_offsets ||
-        !partition_offsets || !workspace)
-        return EP_ERR_INVALID_ARG;
-    if (T > 0) {
-        if (!x || !topk_idx || !is_token_in_partition || !recv_x || !recv_src_token || !dst_row)
-            return EP_ERR_INVALID_ARG;
-        if (fp8 && !recv_scales) return EP_ERR_INVALID_ARG;
-        if (!aligned16(x) || !aligned16(recv_x)) return EP_ERR_INVALID_ARG;
-    }
-    if (num_cus < 0) return EP_ERR_INVALID_ARG;
     const ep::WsMap m = ep::ws_map(T, K, E, P);
     if (workspace_bytes < m.total) return EP_ERR_WORKSPACE;
     return from_hip(ep::launch_layout_dispatch(
@@ -125,6 +186,36 @@ ep_status_t ep_layout_dispatch(const void* x, int32_t num_tokens, int32_t hidden
                                  num_tokens_per_partition, is_token_in_partition, expert_offsets,
                                  partition_offsets, recv_x, recv_scales, recv_src_token, dst_row,
                                  workspace, workspace_bytes, 0, stream);
+}
+
+ep_status_t ep_layout_dispatch_static(const void* x, int32_t num_tokens, int32_t hidden,
+                                      const int64_t* topk_idx, int32_t num_topk,
+                                      int32_t num_experts, int32_t num_partitions,
+                                      ep_dtype_t out_dtype, int32_t* num_tokens_per_expert,
+                                      int32_t* num_tokens_per_partition,
+                                      uint8_t* is_token_in_partition, int32_t* expert_offsets,
+                                      int32_t* partition_offsets, void* recv_x,
+                                      float* recv_scales, int32_t* recv_src_token,
+                                      int32_t* dst_row, void* stream) {
+    const int32_t T = num_tokens, H = hidden, K = num_topk, E = num_experts, P = num_partitions;
+    ep_status_t st = check_layout_dispatch(x, T, H, topk_idx, K, E, P, out_dtype,
+                                           num_tokens_per_expert, num_tokens_per_partition,
+                                           is_token_in_partition, expert_offsets,
+                                           partition_offsets, recv_x, recv_scales,
+                                           recv_src_token, dst_row);
+    if (st != EP_OK) return st;
+    if (ep::ws_map(T, K, E, P).total > (size_t)EP_STATIC_SCRATCH_BYTES) return EP_ERR_UNSUPPORTED;
+    void* ws = nullptr;
+    st = device_scratch(&ws);
+    if (st != EP_OK) return st;
+    // The kernels and outputs of ep_layout_dispatch, with the device's scratch
+    // as the workspace.  Nothing in it needs clearing: every layout call
+    // writes all that its dispatch launch reads.
+    return ep_layout_dispatch_cu(x, num_tokens, hidden, topk_idx, num_topk, num_experts,
+                                 num_partitions, out_dtype, num_tokens_per_expert,
+                                 num_tokens_per_partition, is_token_in_partition, expert_offsets,
+                                 partition_offsets, recv_x, recv_scales, recv_src_token, dst_row,
+                                 ws, (size_t)EP_STATIC_SCRATCH_BYTES, 0, stream);
 }
 
 int64_t ep_aligned_rows(int32_t num_tokens, int32_t num_topk, int32_t num_experts,

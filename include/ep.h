@@ -20,9 +20,11 @@
  * Conventions shared by every entry point:
  *  - Array arguments are device pointers on the current HIP device, row-major
  *    and contiguous, owned by the caller.  The library never allocates or
- *    frees memory; apart from the caller's workspace it keeps no device state
- *    (its only global is a per-device host flag, set once and thread-safe,
- *    recording that a kernel's larger dynamic-LDS limit has been raised).
+ *    frees memory.  Its only device state is the static scratch array of
+ *    ep_layout_dispatch_static (one per GPU); every other call works in the
+ *    caller's workspace.  Its host-side globals are a per-device flag, set
+ *    once and thread-safe, recording that a kernel's larger dynamic-LDS
+ *    limit has been raised, and the per-device address of that scratch.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued asynchronously; nothing synchronises except
  *    ep_get_device_error.
@@ -73,6 +75,7 @@ typedef enum EP_ENUM_BASE {
 #define EP_MAX_TOPK 64
 #define EP_LL_MAX_SLOTS 8192   /* T*K of one ep_low_latency_dispatch call */
 #define EP_MAX_EXPERT_ALIGNMENT 1024   /* of ep_layout_dispatch_aligned */
+#define EP_STATIC_SCRATCH_BYTES (8u << 20)   /* per GPU, of ep_layout_dispatch_static */
 
 /*
  * Bytes of device workspace that ep_get_dispatch_layout and ep_dispatch need
@@ -161,6 +164,35 @@ ep_status_t ep_layout_dispatch(const void *x, int32_t num_tokens, int32_t hidden
                                int32_t *partition_offsets, void *recv_x, float *recv_scales,
                                int32_t *recv_src_token, int32_t *dst_row, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/*
+ * ep_layout_dispatch for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments (minus the workspace), same checks, kernels and
+ * outputs as ep_layout_dispatch; the workspace is instead a static device
+ * array inside the library, EP_STATIC_SCRATCH_BYTES on every GPU that the
+ * library runs on, held until the process ends.  Nothing is allocated; the
+ * caller passes every input and output.  The first call on a device looks up
+ * that device's copy of the array (hipGetSymbolAddress) and keeps its address.
+ *   EP_ERR_UNSUPPORTED when ep_workspace_bytes(T, K, E, P) exceeds
+ *   EP_STATIC_SCRATCH_BYTES (about T*K <= 1M slots at E <= 256), or when the
+ *   current device's index is 64 or more.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind: calls that overlap on one GPU (on different streams without
+ * ordering between them, or from host threads that do not order them) race
+ * and give undefined results; order them on one stream or with events.  The
+ * invalid-id count of a call stays in the array and is not reported
+ * (ep_layout_dispatch with a workspace and ep_get_device_error report it).
+ */
+ep_status_t ep_layout_dispatch_static(const void *x, int32_t num_tokens, int32_t hidden,
+                                      const int64_t *topk_idx, int32_t num_topk,
+                                      int32_t num_experts, int32_t num_partitions,
+                                      ep_dtype_t out_dtype, int32_t *num_tokens_per_expert,
+                                      int32_t *num_tokens_per_partition,
+                                      uint8_t *is_token_in_partition, int32_t *expert_offsets,
+                                      int32_t *partition_offsets, void *recv_x,
+                                      float *recv_scales, int32_t *recv_src_token,
+                                      int32_t *dst_row, void *stream);
 
 /*
  * Receive rows of ep_layout_dispatch_aligned: T*K + E*(expert_alignment-1),

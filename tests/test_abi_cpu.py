@@ -147,6 +147,31 @@ def test_layout_dispatch_rejects_bad_arguments(buf):
     assert call(wsz=128) == WORKSPACE
 
 
+def test_layout_dispatch_static_rejects_bad_arguments(buf):
+    """The no-allocation entry point checks its arguments like
+    ep_layout_dispatch and refuses shapes whose workspace would not fit its
+    static scratch -- all before touching the device."""
+    L = b.lib()
+    x, idx, ce, cp, ip, oe, op, rx, rs, src, dst = (buf() for _ in range(11))
+
+    def call(x=x, T=4, H=256, idx=idx, K=2, E=4, P=2, dt=0, ce=ce, cp=cp, ip=ip, oe=oe, op=op,
+             rx=rx, rs=rs, src=src, dst=dst):
+        return L.ep_layout_dispatch_static(x, T, H, idx, K, E, P, dt, ce, cp, ip, oe, op, rx, rs,
+                                           src, dst, None)
+
+    for kw in [dict(x=None), dict(idx=None), dict(ce=None), dict(cp=None), dict(ip=None),
+               dict(oe=None), dict(op=None), dict(rx=None), dict(src=None), dict(dst=None),
+               dict(H=0), dict(H=12), dict(dt=2), dict(dt=1, H=136),
+               dict(dt=1, rs=None), dict(E=6, P=4), dict(K=5), dict(T=-3),
+               dict(x=ctypes.c_void_p(0x100008)), dict(rx=ctypes.c_void_p(0x100004))]:
+        assert call(**kw) == INVALID, kw
+    assert call(E=2048, P=2) == UNSUPPORTED
+    # 8 MiB of scratch: T = 65536 tokens at top-8 of 256 experts fit, 2^18 do not
+    assert L.ep_workspace_bytes(65536, 8, 256, 64) <= 8 << 20
+    assert L.ep_workspace_bytes(1 << 18, 8, 256, 64) > 8 << 20
+    assert call(T=1 << 18, K=8, E=256, P=64) == UNSUPPORTED
+
+
 def test_dispatch_dedup_rejects_bad_arguments(buf):
     L = b.lib()
     ws = buf(1 << 16)
