@@ -46,9 +46,10 @@ __device__ __forceinline__ int partition_of_expert(int e, uint64_t pmagic) {
 
 // One lane's share of one chunk of a token, ready to store.  FP8 (1024-channel
 // chunks): lane l holds the 16 codes of channels [16l, 16l + 16) of the chunk
-// (its 128-channel group is lanes 8g .. 8g+7; the group's scale goes to
-// s_scale).  bf16 (512-channel chunks): lane l holds channels [8l, 8l + 8) in
-// .a, so every load and store instruction covers 1 KiB of consecutive bytes.
+// in .a (its 128-channel group is lanes 8g .. 8g+7; the group's scale goes to
+// s_scale and, as bits, to .b.x).  bf16 (512-channel chunks): lane l holds
+// channels [8l, 8l + 8) in .a, so every load and store instruction covers
+// 1 KiB of consecutive bytes.
 struct ChunkData {
     uint4 a, b;
 };
@@ -109,7 +110,7 @@ __device__ __forceinline__ ChunkData finish_chunk(const ChunkData& raw, int H, i
         d.a.y = e4m3x4_hw(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
         d.a.z = e4m3x4_hw(f[8] * inv, f[9] * inv, f[10] * inv, f[11] * inv);
         d.a.w = e4m3x4_hw(f[12] * inv, f[13] * inv, f[14] * inv, f[15] * inv);
-        d.b = make_uint4(0, 0, 0, 0);
+        d.b = make_uint4(__float_as_uint(scale), 0, 0, 0);
         if (h0 < H && (lane & 7) == 0) s_scale[h0 >> 7] = scale;
         return d;
     }
@@ -146,6 +147,21 @@ __device__ __forceinline__ void store_chunk(const ChunkData& d, int H, int K, in
             if (r < 0) continue;
             if (act) store_wt(static_cast<uint16_t*>(recv_x) + (int64_t)r * H + h0, d.a);
         }
+    }
+}
+
+// FP8: the scales of one chunk (8 groups, held by lanes 0, 8, ..., 56) to the
+// K destination rows, one 32-byte store per row -- for a wave that writes its
+// chunk's scales itself instead of gathering the token's row in LDS.
+__device__ __forceinline__ void store_chunk_scales(const ChunkData& d, int H, int K, int c,
+                                                   int drow, float* __restrict__ recv_scales) {
+    const int lane = threadIdx.x & 63;
+    const int h0 = c * kDispatchChunk + lane * 16;
+    const bool act = h0 < H && (lane & 7) == 0;
+    const int G = H >> 7;
+    for (int k = 0; k < K; ++k) {
+        const int r = __builtin_amdgcn_readlane(drow, k);
+        if (r >= 0 && act) recv_scales[(int64_t)r * G + (h0 >> 7)] = __uint_as_float(d.b.x);
     }
 }
 
@@ -551,18 +567,24 @@ __global__ void dedup_empty_kernel(int P, int32_t* __restrict__ ptok_off) {
 // dropped).  No row number depends on another expert's count, so nothing has
 // to be summed over all experts before data moves: every workgroup reads the
 // whole (small) routing tensor, builds in LDS the per-expert counts of all
-// slots and of the slots of earlier tokens, takes its own rows from the
-// latter, and then scatters its token exactly as dispatch_kernel does.
-// Workgroup b also writes the counts of experts b, b + grid, ... and marks
-// their unfilled rows with -1, so the whole result comes from this launch.
-// Each workgroup reads T*K routing entries, so the cost grows as T^2*K: this
-// is the small-batch path.
+// slots and of the slots of earlier tokens, takes its token's rows from the
+// latter, and then scatters its share of the token with the same load,
+// quantise and store helpers as dispatch_kernel.  A token's row is split
+// over `split` workgroups (workgroup b takes token b / split and the b % split-th
+// contiguous range of its channel chunks, with the matching scale groups):
+// with fewer tokens than CUs this spreads the stores over more CUs, whose
+// individual store rate is what bounds a small batch.  Workgroup b also
+// writes the counts of experts b, b + grid, ... and marks their unfilled rows
+// with -1, so the whole result comes from this launch.  Each workgroup reads
+// T*K routing entries, so the cost grows as T^2*K*split: this is the
+// small-batch path.
 template <bool FP8>
 __global__ __launch_bounds__(kDispatchMaxThreads) void ll_dispatch_kernel(
     const uint16_t* __restrict__ x, const int64_t* __restrict__ idx, int T, int H, int K, int E,
     int C, int32_t* __restrict__ cnt_e, void* __restrict__ recv_x,
     float* __restrict__ recv_scales, int32_t* __restrict__ recv_src,
-    int32_t* __restrict__ dst_row, int64_t* __restrict__ num_invalid, int nchunk) {
+    int32_t* __restrict__ dst_row, int64_t* __restrict__ num_invalid, int nchunk, int split,
+    int cps) {
     extern __shared__ EP_LDS_ALIGN int smem[];
     int* h_pre = smem;                                      // [E] slots of tokens < t
     int* h_all = smem + E;                                  // [E] all valid slots
@@ -572,7 +594,10 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void ll_dispatch_kernel(
     const int nthr = blockDim.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int t = blockIdx.x;
+    const int t = blockIdx.x / split;
+    const int part = blockIdx.x - t * split;   // this workgroup's share of the token
+    const int c0 = part * cps;                 // its chunks [c0, c1)
+    const int c1 = min(c0 + cps, nchunk);
 
     // This token's own ids (lane k holds slot k) and the first round of the
     // routing scan are loaded together (T >= 1 here and t < T; branch-free,
@@ -590,6 +615,13 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void ll_dispatch_kernel(
         v[j] = idx[i < n ? i : n - 1];
         if (i >= n) v[j] = -1;
     }
+    // The wave's first chunk of the token is requested right after the
+    // routing loads, so that its latency overlaps the scan (branch-free,
+    // in-bounds loads).  (Issued after the histograms, the loads left the
+    // kernel 1.5 us longer at 128 tokens x 7168, top-8 of 256 experts.)
+    const int cfirst = c0 + wave;
+    ChunkData raw;
+    if (cfirst < c1) raw = load_raw<FP8>(x, H, t, cfirst);
 
     for (int e = tid; e < E; e += nthr) {
         h_pre[e] = 0;
@@ -640,7 +672,7 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void ll_dispatch_kernel(
             const int r = h_pre[e] + dup;
             if (r < C) drow = e * C + r;
         }
-        if (wave == 0 && lane < K) {
+        if (part == 0 && wave == 0 && lane < K) {
             dst_row[(int64_t)t * K + lane] = drow;
             if (drow >= 0) recv_src[drow] = t;
         }
@@ -653,9 +685,16 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void ll_dispatch_kernel(
     }
     if (blockIdx.x == 0 && tid == 0 && num_invalid) *num_invalid = s_inv;
 
-    ChunkData first;
-    if (wave < nchunk) first = load_chunk<FP8>(x, H, t, wave, s_scale);
-    scatter_token<FP8>(x, H, K, t, drow, first, recv_x, recv_scales, s_scale, nchunk);
+    // This workgroup's chunks c0 .. c1-1: wave w takes c0 + w, c0 + w + nw,
+    // ...  FP8: each wave writes its own chunk's scales (no barrier and no
+    // LDS round trip, which the decode batch's latency would pay for).
+    const int nw = nthr >> 6;
+    for (int c = cfirst; c < c1; c += nw) {
+        const ChunkData d = finish_chunk<FP8>(c == cfirst ? raw : load_raw<FP8>(x, H, t, c), H,
+                                              c, s_scale);
+        store_chunk<FP8>(d, H, K, c, drow, recv_x);
+        if constexpr (FP8) store_chunk_scales(d, H, K, c, drow, recv_scales);
+    }
 }
 
 // T = 0: every count is 0, every row unfilled, nothing invalid.
@@ -714,15 +753,22 @@ hipError_t launch_ll_dispatch(const uint16_t* x, const int64_t* idx, int T, int 
                            E, C, cnt_e, recv_src, num_invalid);
         return hipGetLastError();
     }
-    const unsigned grid = (unsigned)T;
+    // Workgroups per token: enough to put every CU to work when the batch is
+    // small, each with at least one chunk (cps chunks each, the last fewer).
+    int split = kLlTargetWorkgroups / T;
+    if (split > nchunk) split = nchunk;
+    if (split < 1) split = 1;
+    const int cps = (nchunk + split - 1) / split;
+    split = (nchunk + cps - 1) / cps;
+    const unsigned grid = (unsigned)((int64_t)T * split);
     if (fp8)
         hipLaunchKernelGGL(ll_dispatch_kernel<true>, dim3(grid), dim3(64 * nw), lds, s, x, idx, T,
                            H, K, E, C, cnt_e, recv_x, recv_scales, recv_src, dst_row,
-                           num_invalid, nchunk);
+                           num_invalid, nchunk, split, cps);
     else
         hipLaunchKernelGGL(ll_dispatch_kernel<false>, dim3(grid), dim3(64 * nw), lds, s, x, idx,
                            T, H, K, E, C, cnt_e, recv_x, recv_scales, recv_src, dst_row,
-                           num_invalid, nchunk);
+                           num_invalid, nchunk, split, cps);
     return hipGetLastError();
 }
 

@@ -167,14 +167,19 @@ hipError_t launch_layout_dispatch(const uint16_t* x, const int64_t* idx, int T, 
                                   float* recv_scales, int32_t* recv_src, int32_t* dst_row,
                                   int num_cus, hipStream_t s);
 
-// Fixed-capacity (decode) dispatch: one launch, one workgroup per token (T = 0
-// takes a small fill kernel instead) of kLlWaves waves, so that the routing scan every
-// workgroup does needs few rounds of loads (kLlScanUnroll in flight per
-// thread: one round up to 4096 slots); waves past the token's channel chunks
-// only take part in the scan.  LDS: two [E] int histograms and, for FP8, the
-// token's G scales.
-constexpr int kLlWaves = 16;
+// Fixed-capacity (decode) dispatch: one launch, one or more workgroups per
+// token (T = 0 takes a small fill kernel instead) of kLlWaves waves; the
+// routing scan that every workgroup does takes few rounds of loads
+// (kLlScanUnroll in flight per thread: one round up to 2048 slots), and
+// waves past the workgroup's channel chunks only take part in the scan.
+// Eight waves rather than sixteen start sooner and scan sooner (the kernel
+// ended 0.3 us earlier at 128 tokens x 7168, top-8 of 256 experts).  LDS:
+// two [E] int histograms and, for FP8, the token's G scales.
+constexpr int kLlWaves = 8;
 constexpr int kLlScanUnroll = 4;
+// Workgroups the decode dispatch aims for (one per CU of MI355X): a batch of
+// T < this many tokens splits each token over up to this / T workgroups.
+constexpr int kLlTargetWorkgroups = 256;
 
 size_t ll_dispatch_lds_bytes(int E, int H, bool fp8);
 

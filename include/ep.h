@@ -403,9 +403,11 @@ ep_status_t ep_convert_e4m3(const float *in, uint8_t *out, int64_t n, int32_t mo
  * ep_combine uses.  in fp32 [n], out uint16 [n]. */
 ep_status_t ep_convert_bf16(const float *in, uint16_t *out, int64_t n, void *stream);
 
-/* Plain streaming copy of `bytes` bytes (multiple of 16, 16-byte aligned
- * pointers): reads `bytes` and writes `bytes`.  Used as the reference kernel
- * for HBM traffic counters and the measured copy ceiling. */
+/* Streaming copy of `bytes` bytes (multiple of 16, 16-byte aligned pointers,
+ * non-overlapping): reads `bytes` and writes `bytes`, each wave moving whole
+ * 4 KiB spans with non-temporal 16-byte loads and stores.  Used as the
+ * reference kernel for HBM traffic counters and as the measured copy
+ * ceiling. */
 ep_status_t ep_copy(const void *src, void *dst, size_t bytes, void *stream);
 
 #ifdef __cplusplus

@@ -77,3 +77,19 @@ def test_bf16_conversion_matches_oracle():
     want = oracle.bf16_rne(v)
     bad = np.nonzero(got != want)[0]
     assert bad.size == 0, [(float(v[i]), hex(got[i]), hex(want[i])) for i in bad[:10]]
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 4096 + 16, 3 * 4096 - 16, (1 << 20) + 48,
+                                    (64 << 20) + 4080, 1 << 30])
+def test_copy_is_exact_and_stays_in_bounds(nbytes):
+    """ep_copy (the counters' reference kernel and the copy ceiling) copies
+    every byte, whole 4 KiB spans and the partial last one alike, and writes
+    nothing past the end."""
+    announce("ep_copy %d bytes" % nbytes)
+    g = torch.Generator(device="cuda").manual_seed(nbytes)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+    dst = torch.full((nbytes + 4096,), 0xA5, dtype=torch.uint8, device="cuda")
+    ep.copy(src, dst[:nbytes])
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src)
+    assert bool((dst[nbytes:] == 0xA5).all())
