@@ -83,11 +83,11 @@ __device__ __forceinline__ uint32_t e4m3x4_sw(float a, float b, float c, float d
     return e4m3_sw(a) | (e4m3_sw(b) << 8) | (e4m3_sw(c) << 16) | (e4m3_sw(d) << 24);
 }
 
-// Maximum over the 8 lanes of an aligned group of 8 (lanes 8g .. 8g+7).
-__device__ __forceinline__ float group8_max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 1));
-    v = fmaxf(v, __shfl_xor(v, 2));
-    v = fmaxf(v, __shfl_xor(v, 4));
+// Unsigned maximum over the 8 lanes of an aligned group of 8.
+__device__ __forceinline__ uint32_t group8_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__shfl_xor((int)v, 1));
+    v = max(v, (uint32_t)__shfl_xor((int)v, 2));
+    v = max(v, (uint32_t)__shfl_xor((int)v, 4));
     return v;
 }
 

@@ -80,8 +80,30 @@ __device__ __forceinline__ ChunkData load_raw(const uint16_t* __restrict__ x, in
     return d;
 }
 
+// Largest of the 16 bf16 magnitudes (sign bit cleared) packed in w, as bits:
+// for non-negative values integer order is numeric order, and NaNs (above
+// 0x7F80 = +inf) come out above every number.  With nan_out, NaNs count as 0.
+__device__ __forceinline__ uint32_t max_bf16_magnitude(const uint32_t (&w)[8], bool nan_out) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
+        if (nan_out) {
+            lo = lo > 0x7F80u ? 0u : lo;
+            hi = hi > 0x7F80u ? 0u : hi;
+        }
+        m = max(m, max(lo, hi));
+    }
+    return m;
+}
+
 // Raw words -> what store_chunk writes: the E4M3 codes in .a (and the group
-// scale in s_scale) for FP8; unchanged for bf16.
+// scale in s_scale) for FP8; unchanged for bf16.  A group that holds an
+// infinity or a NaN (rare; found from the integer maximum of its magnitudes)
+// takes a slower path: its maximum leaves the NaNs out (an infinity makes the
+// scale +inf and the inverse 0, so its finite values become signed zeros),
+// and every infinite or NaN x gets the NaN code S.1111.111 with the sign of
+// x, whatever sign the hardware gives the NaN of x * inv.
 template <bool FP8>
 __device__ __forceinline__ ChunkData finish_chunk(const ChunkData& raw, int H, int c,
                                                   float* s_scale) {
@@ -98,10 +120,12 @@ __device__ __forceinline__ ChunkData finish_chunk(const ChunkData& raw, int H, i
             f[2 * i] = bf16_lo(w[i]);
             f[2 * i + 1] = bf16_hi(w[i]);
         }
-        float amax = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-        amax = group8_max(amax);
+        // the group's largest |x| as bf16 bits (exact); the 8 lanes of a
+        // group agree on `finite`, so the branches below split whole groups
+        uint32_t mbits = group8_max_u32(max_bf16_magnitude(w, false));
+        const bool finite = mbits < 0x7F80u;
+        if (!finite) mbits = group8_max_u32(max_bf16_magnitude(w, true));
+        const float amax = __uint_as_float(mbits << 16);
         const float ac = fmaxf(amax, 1e-4f);
         const float inv = 448.0f / ac;
         const float scale = ac / 448.0f;
@@ -110,6 +134,19 @@ __device__ __forceinline__ ChunkData finish_chunk(const ChunkData& raw, int H, i
         d.a.y = e4m3x4_hw(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
         d.a.z = e4m3x4_hw(f[8] * inv, f[9] * inv, f[10] * inv, f[11] * inv);
         d.a.w = e4m3x4_hw(f[12] * inv, f[13] * inv, f[14] * inv, f[15] * inv);
+        if (!finite) {
+            uint32_t q[4] = {d.a.x, d.a.y, d.a.z, d.a.w};
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint32_t b = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                if ((b & 0x7F80u) == 0x7F80u) {             // infinite or NaN x
+                    const uint32_t code = ((b >> 8) & 0x80u) | 0x7Fu;
+                    const int sh = 8 * (i & 3);
+                    q[i >> 2] = (q[i >> 2] & ~(0xFFu << sh)) | (code << sh);
+                }
+            }
+            d.a = make_uint4(q[0], q[1], q[2], q[3]);
+        }
         d.b = make_uint4(__float_as_uint(scale), 0, 0, 0);
         if (h0 < H && (lane & 7) == 0) s_scale[h0 >> 7] = scale;
         return d;

@@ -143,16 +143,25 @@ def make(name: str, T: int | None = None, with_y: bool = True) -> Workload:
     return Workload(name, T, H, cfg["E"], cfg["P"], K, cfg["fp8"], idx, w, x, y, meta)
 
 
+# Non-finite bf16 patterns: +-inf, quiet NaNs and NaNs whose fp32 widening is
+# signalling, of both signs and several payloads.
+NONFINITE_BF16 = np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC0, 0x7F81, 0xFF81, 0x7FA5, 0xFFFF],
+                          np.uint16)
+
+
 def random_case(T: int, H: int, E: int, P: int, K: int, seed: int, *,
                 masked_frac: float = 0.0, invalid_frac: float = 0.0,
                 allow_dup: bool = False, skew: float = 0.0, fp8: bool = False,
-                with_y: bool = True) -> Workload:
+                with_y: bool = True, nonfinite_frac: float = 0.0) -> Workload:
     """A generic seeded case for edge and ragged-shape tests.
 
     Experts are drawn without replacement per token unless ``allow_dup``;
     ``skew`` > 0 biases the draw towards low expert ids (weights 1/(e+1)^skew);
     ``masked_frac`` of the slots become -1 and ``invalid_frac`` become
-    out-of-range ids (E + j or -2 - j).
+    out-of-range ids (E + j or -2 - j).  ``nonfinite_frac`` of the values of x
+    become infinities or NaNs (NONFINITE_BF16), and then token 0's first 128
+    channels are all NaNs (alternating signs) and token 1's first channel is
+    +inf.
     """
     rng = _rng(seed)
     p = 1.0 / np.arange(1, E + 1, dtype=np.float64) ** skew
@@ -171,4 +180,10 @@ def random_case(T: int, H: int, E: int, P: int, K: int, seed: int, *,
     x = bf16_bits_from_f32(rng.standard_normal((T, H), dtype=np.float32))
     y = (bf16_bits_from_f32(rng.standard_normal((T * K, H), dtype=np.float32))
          if with_y else None)
+    if nonfinite_frac > 0:
+        hit = rng.random((T, H)) < nonfinite_frac
+        x[hit] = NONFINITE_BF16[rng.integers(0, NONFINITE_BF16.size, int(hit.sum()))]
+        x[0, :min(128, H)] = np.where(np.arange(min(128, H)) % 2 == 0, 0x7FC1, 0xFFA0)
+        if T > 1:
+            x[1, 0] = 0x7F80
     return Workload("random", T, H, E, P, K, fp8, idx, w, x, y, {"seed": seed})

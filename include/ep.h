@@ -134,7 +134,10 @@ ep_status_t ep_get_dispatch_layout(const int64_t *topk_idx, int32_t num_tokens,
  *     to nearest even, saturating, sign kept); recv_x is uint8 [R*H] and
  *     recv_scales fp32 [R*G] holds s, so x ~= code * s.  (FP8 for dispatch:
  *     feature list of "DeepSeek Open Source Weekly Review - 2"; the format,
- *     granularity and scale rule are this library's.)
+ *     granularity and scale rule are this library's.)  Non-finite x: a NaN
+ *     takes no part in the maximum a; an infinity makes s = +inf and 448/a_c
+ *     = 0, so the group's finite values get signed-zero codes; every infinite
+ *     or NaN x gets the code S.1111.111 (0x7F / 0xFF) with the sign of x.
  * x is bf16 [T*H]; topk_idx int64 [T*K] and workspace must be the ones the
  * preceding ep_get_dispatch_layout call used, with the same T, K, E, P and on
  * the same stream (or ordered after it).  H % 8 == 0.
@@ -298,7 +301,9 @@ ep_status_t ep_dispatch_dedup(const void *x, int32_t num_tokens, int32_t hidden,
  * no y row outside the buffer is ever read.  topk_weights fp32 [T*K]; out
  * bf16 [T*H].  H % 8 == 0.  T may be 0.  (The weighting and the fp32
  * accumulation order are this library's reading; the pages only name the
- * operation.)
+ * operation.)  y and topk_weights are expected finite: with an infinity or a
+ * NaN the result is the IEEE result of the same chain (NaN, +-inf), with the
+ * sign and payload of a NaN unspecified.
  */
 ep_status_t ep_combine(const void *y, int64_t num_rows, const int32_t *dst_row,
                        const float *topk_weights, int32_t num_tokens, int32_t num_topk,

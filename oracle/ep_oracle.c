@@ -266,6 +266,12 @@ void oracle_dispatch_bf16(const uint16_t *x, int32_t T, int32_t H,
  *   s    = a_c / 448.0f           (one correctly rounded fp32 division)
  *   q[h] = E4M3(x[h] * inv)       (one rounded fp32 product, then encode)
  *   q [T][H] bytes, s [T][H/128] fp32.  H must be a multiple of 128.
+ * Non-finite x (the pages say nothing of them; this reading keeps the sign
+ * of x in every code, as for zeros): a NaN is left out of the maximum (the
+ * comparison below is false for it), an infinity makes a = a_c = s = +inf
+ * and inv = 0, and the code of an infinite or NaN x is the NaN pattern
+ * S.1111.111 with S the sign of x -- x * inv is a NaN for both, and IEEE
+ * arithmetic leaves open the sign of the NaN that inf * 0 produces.
  */
 void oracle_quantize(const uint16_t *x, int32_t T, int32_t H, uint8_t *q, float *s)
 {
@@ -282,8 +288,11 @@ void oracle_quantize(const uint16_t *x, int32_t T, int32_t H, uint8_t *q, float 
             float inv = 448.0f / ac;
             s[t * G + g] = ac / 448.0f;
             for (int32_t j = 0; j < 128; ++j) {
-                float prod = bf16_to_f32(x[t * H + 128 * g + j]) * inv;
-                q[t * H + 128 * g + j] = oracle_e4m3(prod);
+                float xv = bf16_to_f32(x[t * H + 128 * g + j]);
+                if (isnan(xv) || isinf(xv))
+                    q[t * H + 128 * g + j] = signbit(xv) ? 0xFFu : 0x7Fu;
+                else
+                    q[t * H + 128 * g + j] = oracle_e4m3(xv * inv);
             }
         }
     }

@@ -1,9 +1,12 @@
 """The device conversions, value by value, against the oracle (GPU).
 
 E4M3: the dispatch kernel's hardware conversion (v_cvt_pk_fp8_f32) over the
-inputs the quantiser can produce (|v| < 464: every bf16 value times a set of
-scales, a dense sweep, every midpoint between codes and its fp32 neighbours),
-and the software conversion over every finite value.  bf16: the combine
+inputs the quantiser hands it (finite, |v| < 464: every bf16 value times a set
+of scales, a dense sweep, every midpoint between codes and its fp32
+neighbours) -- the quantiser never converts a non-finite product, it writes
+the NaN code of an infinite or NaN x itself (tests/test_gpu_parity.py covers
+those tokens) -- and the software conversion over every finite value plus
+infinities and NaNs of both signs and several payloads.  bf16: the combine
 kernel's rounding over random bit patterns and exact ties.
 """
 import numpy as np
@@ -56,7 +59,9 @@ def test_e4m3_software_conversion_matches_oracle():
     v = _e4m3_inputs()
     rng = np.random.default_rng(1)
     rnd = rng.integers(0, 2 ** 32, 1_000_000, dtype=np.uint64).astype(np.uint32).view(np.float32)
-    v = np.concatenate([v, rnd[np.isfinite(rnd)]])
+    nonfinite = np.array([0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00000, 0x7F800001,
+                          0xFF800001, 0x7FA5A5A5, 0xFFFFFFFF], np.uint32).view(np.float32)
+    v = np.concatenate([v, rnd[np.isfinite(rnd)], nonfinite])
     announce("convert_e4m3 sw n=%d" % v.size)
     got = ep.convert_e4m3(torch.from_numpy(v).cuda(), mode=1).cpu().numpy()
     want = oracle.e4m3(v)

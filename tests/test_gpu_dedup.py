@@ -115,6 +115,7 @@ CASES = [
     (9000, 128, 256, 64, 8, 65, dict(masked_frac=0.02, invalid_frac=0.01)),
     (70, 17536, 64, 8, 8, 69, dict(fp8=True, masked_frac=0.05)),   # waves loop over chunks
     (66, 18440, 32, 4, 6, 70, dict(allow_dup=True)),
+    (300, 1024, 64, 8, 6, 71, dict(fp8=True, nonfinite_frac=0.01)),   # infinities and NaNs in x
 ]
 
 

@@ -117,6 +117,8 @@ LL_CASES = [
     (33, 2048, 1, 1, 40, 10, dict()),                                # one expert
     (70, 17536, 64, 8, 16, 11, dict(fp8=True, masked_frac=0.05)),    # waves loop over chunks
     (66, 18440, 32, 6, 20, 12, dict(allow_dup=True)),
+    (96, 2048, 64, 6, 24, 13, dict(fp8=True, nonfinite_frac=0.01)),   # infinities and NaNs in x
+    (96, 2048, 64, 6, 24, 14, dict(nonfinite_frac=0.01)),
 ]
 
 

@@ -90,6 +90,18 @@ def test_every_slot_masked(one_call):
     assert stats["N"] == 0
 
 
+@pytest.mark.parametrize("one_call", [False, True], ids=["two_calls", "one_call"])
+@pytest.mark.parametrize("fp8", [True, False], ids=["fp8", "bf16"])
+def test_nonfinite_tokens(fp8, one_call):
+    """Infinities and NaNs of both signs in x (1% of the values, an all-NaN
+    group, groups with an infinity): FP8 codes and scales bit-exact with the
+    oracle's reading (NaNs left out of the group maximum, an infinity giving
+    scale +inf and signed zeros, S.1111.111 with the sign of x for every
+    non-finite x), bf16 rows bitwise copies."""
+    case = wl.random_case(700, 1024, 64, 8, 6, 31, fp8=fp8, nonfinite_frac=0.01)
+    check_case(case, label="non-finite x", one_call=one_call)
+
+
 def test_invalid_ids_are_counted():
     case = wl.random_case(900, 128, 64, 8, 4, 23, invalid_frac=0.05, masked_frac=0.05)
     n_bad = int(((case.topk_idx != -1) & ((case.topk_idx < 0) | (case.topk_idx >= 64))).sum())

@@ -28,6 +28,9 @@ LAYOUT = [lambda: pins.test_layout_hand_worked(GOLDEN),
           pins.test_layout_invalid_ids_are_masked_and_counted]
 QUANT = [pins.test_quantize_matches_numpy_steps_and_invariants,
          pins.test_fp8_dispatch_rows_are_quantised_tokens]
+# Non-finite tokens in the quantiser.
+QUANT_NONFINITE = [lambda: pins.test_quantize_hand_worked_nonfinite_groups(GOLDEN),
+                   pins.test_quantize_nonfinite_invariants]
 # The quantiser's two divisions, pinned without the numpy restatement of its steps.
 QUANT_EXACT = [lambda: pins.test_quantize_hand_worked_scale_groups(GOLDEN),
                pins.test_quantize_exact_rational]
@@ -97,6 +100,12 @@ MUTANTS = [
      "float inv = 448.0f * (1.0f / ac);", QUANT_EXACT),
     ("scale multiplies by a reciprocal", "s[t * G + g] = ac / 448.0f;",
      "s[t * G + g] = ac * (1.0f / 448.0f);", QUANT_EXACT),
+    ("non-finite codes lose the sign of x", "q[t * H + 128 * g + j] = signbit(xv) ? 0xFFu : 0x7Fu;",
+     "q[t * H + 128 * g + j] = 0x7Fu;", QUANT_NONFINITE),
+    ("NaN taken into the maximum", "                if (v > a)\n                    a = v;",
+     "                if (v > a || isnan(v))\n                    a = v;", QUANT_NONFINITE),
+    ("non-finite x encoded from the product", "                if (isnan(xv) || isinf(xv))",
+     "                if (isnan(xv))", QUANT_NONFINITE),
     ("amax floor dropped", "float ac = (a > 1e-4f) ? a : 1e-4f;", "float ac = a;", QUANT),
     ("amax without abs", "float v = fabsf(bf16_to_f32(x[t * H + 128 * g + j]));",
      "float v = bf16_to_f32(x[t * H + 128 * g + j]);", QUANT),
@@ -150,6 +159,7 @@ MUTANTS = [
 
 
 GROUPS = {"E4M3": E4M3, "BF16": BF16, "LAYOUT": LAYOUT, "QUANT": QUANT, "QUANT_EXACT": QUANT_EXACT,
+          "QUANT_NONFINITE": QUANT_NONFINITE,
           "COMBINE": COMBINE, "DISPATCH": DISPATCH, "LL": LL, "DEDUP": DEDUP,
           "ALIGNED": ALIGNED}
 

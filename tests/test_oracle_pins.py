@@ -662,6 +662,77 @@ def test_quantize_exact_rational():
     assert 10 < n_floor < T - 10
 
 
+def _read_nonfinite_groups(golden_dir):
+    """x [1, 384] bf16 bits, expected codes [1, 384] and scale bits [3] from
+    tests/golden/fp8_nonfinite_hand_worked.txt."""
+    x = np.zeros((1, 384), np.uint16)
+    want_q = np.zeros((1, 384), np.uint8)
+    want_s = np.zeros(3, np.uint32)
+    for line in open(os.path.join(golden_dir, "fp8_nonfinite_hand_worked.txt")):
+        f = line.split()
+        if not f or f[0].startswith("#"):
+            continue
+        g = int(f[1])
+        if f[2] == "ch":
+            x[0, 128 * g + int(f[3])] = int(f[5], 16)
+            want_q[0, 128 * g + int(f[3])] = int(f[7], 16)
+        elif f[2] == "nan_even":
+            even, odd = int(f[3], 16), int(f[5], 16)
+            x[0, 128 * g:128 * g + 128] = np.where(np.arange(128) % 2 == 0, even, odd)
+            want_q[0, 128 * g:128 * g + 128] = np.where(
+                np.arange(128) % 2 == 0, 0x7F | ((even >> 8) & 0x80), 0x7F | ((odd >> 8) & 0x80))
+        else:
+            want_s[g] = int(f[3], 16)
+    return x, want_q, want_s
+
+
+def test_quantize_hand_worked_nonfinite_groups(golden_dir):
+    """Infinities and NaNs in a group, worked by hand
+    (tests/golden/fp8_nonfinite_hand_worked.txt): NaNs left out of the maximum,
+    an infinity giving s = +inf and signed-zero codes for the finite values,
+    and S.1111.111 with the sign of x for every non-finite x."""
+    x, want_q, want_s = _read_nonfinite_groups(golden_dir)
+    q, s = oracle.quantize(x)
+    np.testing.assert_array_equal(q, want_q)
+    np.testing.assert_array_equal(s.reshape(-1).view(np.uint32), want_s)
+
+
+def test_quantize_nonfinite_invariants():
+    """Random groups with infinities and NaNs of both signs (quiet and
+    signalling) dropped in: (i) the code of every non-finite x is 0x7F with
+    the sign of x; (ii) a group with a NaN but no infinity quantises its
+    finite values exactly as the same group with the NaNs replaced by zeros
+    (a NaN takes no part in the maximum); (iii) a group with an infinity has
+    s = +inf and signed zeros for its finite values."""
+    rng = np.random.default_rng(23)
+    T, H = 40, 1024
+    xb = wl.bf16_bits_from_f32(rng.standard_normal((T, H), dtype=np.float32))
+    specials = np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC0, 0x7F81, 0xFFFF, 0x7FA5], np.uint16)
+    hit = rng.random((T, H)) < 0.01
+    hit[:, :128] = False                                   # group 0 of every token stays finite
+    xb[hit] = specials[rng.integers(0, specials.size, hit.sum())]
+    q, s = oracle.quantize(xb)
+    nonfin = (xb & 0x7F80) == 0x7F80
+    sign = (xb >> 8) & 0x80
+    np.testing.assert_array_equal(q[nonfin], (0x7F | sign[nonfin]).astype(np.uint8))
+    xg = xb.reshape(T, H // 128, 128)
+    qg = q.reshape(T, H // 128, 128)
+    is_inf = ((xg & 0x7FFF) == 0x7F80).any(axis=2)
+    is_nan = ((xg & 0x7FFF) > 0x7F80).any(axis=2)
+    assert is_inf.any() and (is_nan & ~is_inf).any()
+    zeroed = np.where((xb & 0x7FFF) > 0x7F80, np.uint16(0), xb)
+    qz, sz = oracle.quantize(zeroed)
+    qzg = qz.reshape(T, H // 128, 128)
+    for t, g in zip(*np.nonzero(is_nan & ~is_inf)):
+        fin = (xg[t, g] & 0x7F80) != 0x7F80
+        np.testing.assert_array_equal(qg[t, g][fin], qzg[t, g][fin])
+        assert s[t, g] == sz[t, g]
+    for t, g in zip(*np.nonzero(is_inf)):
+        fin = (xg[t, g] & 0x7F80) != 0x7F80
+        assert np.isposinf(s[t, g])
+        np.testing.assert_array_equal(qg[t, g][fin], ((xg[t, g][fin] >> 8) & 0x80).astype(np.uint8))
+
+
 def test_fp8_dispatch_rows_are_quantised_tokens():
     c = wl.random_case(70, 384, 16, 4, 3, 11, masked_frac=0.1)
     res = oracle.run(c.topk_idx, c.x_bits, 16, 4, fp8=True)
