@@ -83,11 +83,15 @@ __device__ __forceinline__ uint32_t e4m3x4_sw(float a, float b, float c, float d
     return e4m3_sw(a) | (e4m3_sw(b) << 8) | (e4m3_sw(c) << 16) | (e4m3_sw(d) << 24);
 }
 
-// Unsigned maximum over the 8 lanes of an aligned group of 8.
+// Unsigned maximum over the 8 lanes of an aligned group of 8, with three DPP
+// moves (no LDS round trip): swap neighbours (quad_perm 1,0,3,2), swap pairs
+// (quad_perm 2,3,0,1), then mirror each half row of 8 lanes, which pairs the
+// two quads.  A source lane that is inactive reads as 0, which leaves an
+// unsigned maximum unchanged.
 __device__ __forceinline__ uint32_t group8_max_u32(uint32_t v) {
-    v = max(v, (uint32_t)__shfl_xor((int)v, 1));
-    v = max(v, (uint32_t)__shfl_xor((int)v, 2));
-    v = max(v, (uint32_t)__shfl_xor((int)v, 4));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));
     return v;
 }
 
