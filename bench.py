@@ -128,6 +128,19 @@ def kernel_source_hash(kernel):
     return h.hexdigest()
 
 
+def combine_kernel_name(T, H, K, num_cus):
+    """Name of the kernel ep_combine launches for this shape, for the roofline
+    label: top-8 without a CU budget runs in tiles of min(112 KiB / (2H), 8,
+    T / 512) tokens when that is at least 2; everything else one wave per
+    (token, chunk) task (the budget form under --cu-budget)."""
+    kt = K if K in (1, 2, 4, 6, 8) else 0
+    if num_cus:
+        return "combine_budget_kernel<%d>" % kt
+    if K == 8 and min(112 * 1024 // (2 * H), 8, T // 512) >= 2:
+        return "combine_tile_kernel<8>"
+    return "combine_kernel<%d>" % kt
+
+
 def measured_traffic(kernel, config):
     """HBM bytes per launch from the committed rocprofv3 counter runs, scaled by
     the copy-kernel calibration; None when missing or taken on other code."""
@@ -554,7 +567,7 @@ def main():
     if args.low_latency:
         kname = "ll_dispatch_kernel<%s>" % ("true" if fp8 else "false")
     else:
-        kname = "combine_kernel<%d>" % (K if K in (1, 2, 4, 6, 8) else 0)
+        kname = combine_kernel_name(T, H, K, args.cu_budget)
     roofline = {"bound": "hbm", "kernel": kname,
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -37,6 +37,15 @@ constexpr int kLayoutEntries = 2048;
 // Dynamic LDS the single-launch layout may use (gfx950 gives a workgroup up to
 // 160 KiB; a little is left for the kernel's static LDS).
 constexpr size_t kFusedLdsLimit = 156 * 1024;
+
+// A launch asking for more than 64 KiB of dynamic LDS first raises the
+// kernel's cap (hipFuncAttributeMaxDynamicSharedMemorySize) to `bytes` on the
+// current device, once per (slot, device); each kernel has its own slot.
+constexpr int kFusedLdsSlot = 0;
+constexpr int kCountLdsSlot = 1;          // + count mode (3 slots)
+constexpr int kCombineTileLdsSlot = 4;
+constexpr int kLdsSlots = 5;
+hipError_t allow_large_lds(const void* fn, int slot, int bytes);
 // ... and only for inputs of at most this many token blocks.
 constexpr int kFusedMaxBlocks = 2;
 
@@ -204,6 +213,16 @@ hipError_t launch_dispatch_dedup(const uint16_t* x, const int64_t* idx, int T, i
 // workgroup (measured ~3% faster than 4 or 8 and slightly faster than 1).
 constexpr int kCombineThreads = 128;
 constexpr int kCombineChunk = 512;
+// Tiled form for large top-8 batches: workgroups of 16 waves, each owning a
+// tile of consecutive tokens whose outputs (at most kCombineTileLds bytes,
+// one workgroup per CU) are staged in LDS and written as one burst; used
+// while the batch gives every CU of a 256-CU part at least two tiles.  (Two
+// workgroups per CU, with 72 or 56 KiB tiles, or 8 waves measured slower or
+// no faster.)
+constexpr int kCombineTileK = 8;
+constexpr int kCombineTileThreads = 1024;
+constexpr size_t kCombineTileLds = 112 * 1024;
+constexpr int kCombineTileMinBlocks = 512;
 
 // num_cus > 0: the CU-budget form (at most num_cus workgroups of
 // kBudgetThreads striding over the tasks); otherwise the ordinary launch.

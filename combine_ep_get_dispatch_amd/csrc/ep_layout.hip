@@ -830,17 +830,13 @@ size_t layout_fused_lds_bytes(int T, int K, int E, int P) {
     return sizeof(int) * ((size_t)(4 + kLayoutWaves) * E + kLayoutEntries + P) + ids;
 }
 
-namespace {
-
 // Raising a kernel's dynamic-LDS cap is a per-device attribute of the
 // function: it is set once per (kernel, device) -- remembered in one bit per
-// device of an atomic word per kernel, so concurrent callers and several
-// devices are safe -- to the largest LDS any launch here asks for
-// (kLdsCap).  Devices past 63 set it on every call.
-constexpr int kLdsCap = (int)kFusedLdsLimit;
-constexpr int kFusedLdsSlot = 0;
-constexpr int kCountLdsSlot = 1;   // + count mode
-std::atomic<uint64_t> g_lds_raised[4];
+// device of an atomic word per kernel slot, so concurrent callers and several
+// devices are safe.  Devices past 63 set it on every call.
+namespace {
+std::atomic<uint64_t> g_lds_raised[kLdsSlots];
+}  // namespace
 
 hipError_t allow_large_lds(const void* fn, int slot, int bytes) {
     int dev = 0;
@@ -852,6 +848,9 @@ hipError_t allow_large_lds(const void* fn, int slot, int bytes) {
     return e;
 }
 
+namespace {
+// The layout kernels raise their cap to the largest LDS any launch here asks for.
+constexpr int kLdsCap = (int)kFusedLdsLimit;
 }  // namespace
 
 bool layout_single_launch(int T, int K, int E, int P, const WsMap& m) {

@@ -149,6 +149,24 @@ NONFINITE_BF16 = np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC0, 0x7F81, 0xFF81, 0x7FA
                           np.uint16)
 
 
+def combine_inputs(T: int, H: int, K: int, R: int, seed: int, *, masked_frac: float = 0.0,
+                   past_frac: float = 0.0):
+    """Seeded inputs of a combine alone: y [R, H] bf16 bits, dst_row [T, K]
+    int32 with rows drawn from [0, R) (repeats allowed), ``masked_frac`` of
+    them -1 and ``past_frac`` of them in [R, R + 100) (past the end of y),
+    and topk_weights [T, K] fp32 in [0, 1)."""
+    rng = _rng(seed)
+    y = normal_bf16(seed + 1, (R, H))
+    dst = rng.integers(0, max(R, 1), (T, K)).astype(np.int32)
+    if masked_frac > 0:
+        dst[rng.random((T, K)) < masked_frac] = -1
+    if past_frac > 0:
+        past = rng.random((T, K)) < past_frac
+        dst[past] = (R + rng.integers(0, 100, (T, K))).astype(np.int32)[past]
+    w = rng.random((T, K)).astype(np.float32)
+    return y, dst, w
+
+
 def random_case(T: int, H: int, E: int, P: int, K: int, seed: int, *,
                 masked_frac: float = 0.0, invalid_frac: float = 0.0,
                 allow_dup: bool = False, skew: float = 0.0, fp8: bool = False,
