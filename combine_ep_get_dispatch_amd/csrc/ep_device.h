@@ -9,6 +9,7 @@ namespace ep {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // 16-byte loads and stores with the non-temporal hint, for data that is
@@ -34,6 +35,12 @@ __device__ __forceinline__ void store_nt(void* p, const uint4& v) {
 __device__ __forceinline__ void store_wt(void* p, const uint4& v) {
     const u32x4 w = {v.x, v.y, v.z, v.w};
     asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" : : "v"(p), "v"(w) : "memory");
+}
+
+// The same for 8 bytes (no wait states needed after a store of 8 bytes or less).
+__device__ __forceinline__ void store_wt8(void* p, const uint2& v) {
+    const u32x2 w = {v.x, v.y};
+    asm volatile("global_store_dwordx2 %0, %1, off sc1" : : "v"(p), "v"(w) : "memory");
 }
 
 // bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 word.
@@ -92,6 +99,14 @@ __device__ __forceinline__ uint32_t group8_max_u32(uint32_t v) {
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));
+    return v;
+}
+
+// Unsigned maximum over the 16 lanes of a DPP row: the maximum over each
+// half row, then a row mirror (lane i reads lane 15 - i) pairs the halves.
+__device__ __forceinline__ uint32_t group16_max_u32(uint32_t v) {
+    v = group8_max_u32(v);
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));
     return v;
 }
 

@@ -80,13 +80,14 @@ __device__ __forceinline__ ChunkData load_raw(const uint16_t* __restrict__ x, in
     return d;
 }
 
-// Largest of the 16 bf16 magnitudes (sign bit cleared) packed in w, as bits:
+// Largest of the 2N bf16 magnitudes (sign bit cleared) packed in w, as bits:
 // for non-negative values integer order is numeric order, and NaNs (above
 // 0x7F80 = +inf) come out above every number.  With nan_out, NaNs count as 0.
-__device__ __forceinline__ uint32_t max_bf16_magnitude(const uint32_t (&w)[8], bool nan_out) {
+template <int N>
+__device__ __forceinline__ uint32_t max_bf16_magnitude(const uint32_t (&w)[N], bool nan_out) {
     uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < N; ++i) {
         uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
         if (nan_out) {
             lo = lo > 0x7F80u ? 0u : lo;
@@ -97,13 +98,42 @@ __device__ __forceinline__ uint32_t max_bf16_magnitude(const uint32_t (&w)[8], b
     return m;
 }
 
+// The E4M3 codes of the 2N bf16 values packed in w, each multiplied by inv
+// first (byte j of q[i] = value 4i + j).  Unless the group is finite, every
+// infinite or NaN x gets the NaN code S.1111.111 with the sign of x, whatever
+// sign the hardware gives the NaN of x * inv.
+template <int N>
+__device__ __forceinline__ void e4m3_codes(const uint32_t (&w)[N], float inv, bool finite,
+                                           uint32_t (&q)[N / 2]) {
+    float f[2 * N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        f[2 * i] = bf16_lo(w[i]);
+        f[2 * i + 1] = bf16_hi(w[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i)
+        q[i] = e4m3x4_hw(f[4 * i] * inv, f[4 * i + 1] * inv, f[4 * i + 2] * inv,
+                         f[4 * i + 3] * inv);
+    if (!finite) {
+#pragma unroll
+        for (int i = 0; i < 2 * N; ++i) {
+            const uint32_t b = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+            if ((b & 0x7F80u) == 0x7F80u) {             // infinite or NaN x
+                const uint32_t code = ((b >> 8) & 0x80u) | 0x7Fu;
+                const int sh = 8 * (i & 3);
+                q[i >> 2] = (q[i >> 2] & ~(0xFFu << sh)) | (code << sh);
+            }
+        }
+    }
+}
+
 // Raw words -> what store_chunk writes: the E4M3 codes in .a (and the group
 // scale in s_scale) for FP8; unchanged for bf16.  A group that holds an
 // infinity or a NaN (rare; found from the integer maximum of its magnitudes)
 // takes a slower path: its maximum leaves the NaNs out (an infinity makes the
 // scale +inf and the inverse 0, so its finite values become signed zeros),
-// and every infinite or NaN x gets the NaN code S.1111.111 with the sign of
-// x, whatever sign the hardware gives the NaN of x * inv.
+// and its infinite or NaN values get the NaN code (e4m3_codes).
 template <bool FP8>
 __device__ __forceinline__ ChunkData finish_chunk(const ChunkData& raw, int H, int c,
                                                   float* s_scale) {
@@ -114,42 +144,63 @@ __device__ __forceinline__ ChunkData finish_chunk(const ChunkData& raw, int H, i
         const int h0 = c * kDispatchChunk + lane * 16;
         const uint32_t w[8] = {raw.a.x, raw.a.y, raw.a.z, raw.a.w,
                                raw.b.x, raw.b.y, raw.b.z, raw.b.w};
-        float f[16];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            f[2 * i] = bf16_lo(w[i]);
-            f[2 * i + 1] = bf16_hi(w[i]);
-        }
         // the group's largest |x| as bf16 bits (exact); the 8 lanes of a
-        // group agree on `finite`, so the branches below split whole groups
+        // group agree on `finite`, so the branches split whole groups
         uint32_t mbits = group8_max_u32(max_bf16_magnitude(w, false));
         const bool finite = mbits < 0x7F80u;
         if (!finite) mbits = group8_max_u32(max_bf16_magnitude(w, true));
-        const float amax = __uint_as_float(mbits << 16);
-        const float ac = fmaxf(amax, 1e-4f);
+        const float ac = fmaxf(__uint_as_float(mbits << 16), 1e-4f);
         const float inv = 448.0f / ac;
         const float scale = ac / 448.0f;
+        uint32_t q[4];
+        e4m3_codes(w, inv, finite, q);
         ChunkData d;
-        d.a.x = e4m3x4_hw(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
-        d.a.y = e4m3x4_hw(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
-        d.a.z = e4m3x4_hw(f[8] * inv, f[9] * inv, f[10] * inv, f[11] * inv);
-        d.a.w = e4m3x4_hw(f[12] * inv, f[13] * inv, f[14] * inv, f[15] * inv);
-        if (!finite) {
-            uint32_t q[4] = {d.a.x, d.a.y, d.a.z, d.a.w};
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const uint32_t b = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-                if ((b & 0x7F80u) == 0x7F80u) {             // infinite or NaN x
-                    const uint32_t code = ((b >> 8) & 0x80u) | 0x7Fu;
-                    const int sh = 8 * (i & 3);
-                    q[i >> 2] = (q[i >> 2] & ~(0xFFu << sh)) | (code << sh);
-                }
-            }
-            d.a = make_uint4(q[0], q[1], q[2], q[3]);
-        }
+        d.a = make_uint4(q[0], q[1], q[2], q[3]);
         d.b = make_uint4(__float_as_uint(scale), 0, 0, 0);
         if (h0 < H && (lane & 7) == 0) s_scale[h0 >> 7] = scale;
         return d;
+    }
+}
+
+// The decode dispatch's FP8 chunk is 512 channels (kLlChunk): lane l holds
+// channels [8l, 8l + 8) (one 16-byte load, the bf16 chunk's), its 128-channel
+// group is the 16 lanes of its DPP row, and its 8 codes go out as one 8-byte
+// store per destination.  Half the 1024-channel chunk's quantiser work per
+// wave, so a small batch spreads it over twice as many waves.
+struct HalfChunk {
+    uint2 q;        // the 8 codes
+    float scale;    // the group's scale
+};
+
+__device__ __forceinline__ HalfChunk quantise_half(const uint4& raw) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t mbits = group16_max_u32(max_bf16_magnitude(w, false));
+    const bool finite = mbits < 0x7F80u;
+    if (!finite) mbits = group16_max_u32(max_bf16_magnitude(w, true));
+    const float ac = fmaxf(__uint_as_float(mbits << 16), 1e-4f);
+    uint32_t q[2];
+    e4m3_codes(w, 448.0f / ac, finite, q);
+    HalfChunk d;
+    d.q = make_uint2(q[0], q[1]);
+    d.scale = ac / 448.0f;
+    return d;
+}
+
+// Store a 512-channel FP8 chunk of codes and its 4 group scales to the K
+// destination rows held by lanes 0..K-1 of `drow` (-1 = none).
+__device__ __forceinline__ void store_half_chunk(const HalfChunk& d, int H, int K, int c,
+                                                 int drow, void* __restrict__ recv_x,
+                                                 float* __restrict__ recv_scales) {
+    const int lane = threadIdx.x & 63;
+    const int h0 = c * kLlChunk + lane * 8;
+    const bool act = h0 < H;
+    const bool lead = act && (lane & 15) == 0;
+    const int G = H >> 7;
+    for (int k = 0; k < K; ++k) {
+        const int r = __builtin_amdgcn_readlane(drow, k);
+        if (r < 0) continue;
+        if (act) store_wt8(static_cast<uint8_t*>(recv_x) + (int64_t)r * H + h0, d.q);
+        if (lead) recv_scales[(int64_t)r * G + (h0 >> 7)] = d.scale;
     }
 }
 
@@ -184,21 +235,6 @@ __device__ __forceinline__ void store_chunk(const ChunkData& d, int H, int K, in
             if (r < 0) continue;
             if (act) store_wt(static_cast<uint16_t*>(recv_x) + (int64_t)r * H + h0, d.a);
         }
-    }
-}
-
-// FP8: the scales of one chunk (8 groups, held by lanes 0, 8, ..., 56) to the
-// K destination rows, one 32-byte store per row -- for a wave that writes its
-// chunk's scales itself instead of gathering the token's row in LDS.
-__device__ __forceinline__ void store_chunk_scales(const ChunkData& d, int H, int K, int c,
-                                                   int drow, float* __restrict__ recv_scales) {
-    const int lane = threadIdx.x & 63;
-    const int h0 = c * kDispatchChunk + lane * 16;
-    const bool act = h0 < H && (lane & 7) == 0;
-    const int G = H >> 7;
-    for (int k = 0; k < K; ++k) {
-        const int r = __builtin_amdgcn_readlane(drow, k);
-        if (r >= 0 && act) recv_scales[(int64_t)r * G + (h0 >> 7)] = __uint_as_float(d.b.x);
     }
 }
 
@@ -605,9 +641,10 @@ __global__ void dedup_empty_kernel(int P, int32_t* __restrict__ ptok_off) {
 // to be summed over all experts before data moves: every workgroup reads the
 // whole (small) routing tensor, builds in LDS the per-expert counts of all
 // slots and of the slots of earlier tokens, takes its token's rows from the
-// latter, and then scatters its share of the token with the same load,
-// quantise and store helpers as dispatch_kernel.  A token's row is split
-// over `split` workgroups (workgroup b takes token b / split and the b % split-th
+// latter, and then scatters its share of the token in 512-channel chunks
+// (bf16: dispatch_kernel's chunk; FP8: the half-size chunk of quantise_half,
+// whose group maximum spans a DPP row).  A token's row is split over `split`
+// workgroups (workgroup b takes token b / split and the b % split-th
 // contiguous range of its channel chunks, with the matching scale groups):
 // with fewer tokens than CUs this spreads the stores over more CUs, whose
 // individual store rate is what bounds a small batch.  Workgroup b also
@@ -625,7 +662,6 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void ll_dispatch_kernel(
     extern __shared__ EP_LDS_ALIGN int smem[];
     int* h_pre = smem;                                      // [E] slots of tokens < t
     int* h_all = smem + E;                                  // [E] all valid slots
-    float* s_scale = reinterpret_cast<float*>(smem + 2 * E); // [G] (FP8)
     __shared__ int s_inv;
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;
@@ -658,7 +694,7 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void ll_dispatch_kernel(
     // kernel 1.5 us longer at 128 tokens x 7168, top-8 of 256 experts.)
     const int cfirst = c0 + wave;
     ChunkData raw;
-    if (cfirst < c1) raw = load_raw<FP8>(x, H, t, cfirst);
+    if (cfirst < c1) raw = load_raw<false>(x, H, t, cfirst);   // 512 channels, either dtype
 
     for (int e = tid; e < E; e += nthr) {
         h_pre[e] = 0;
@@ -722,15 +758,17 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void ll_dispatch_kernel(
     }
     if (blockIdx.x == 0 && tid == 0 && num_invalid) *num_invalid = s_inv;
 
-    // This workgroup's chunks c0 .. c1-1: wave w takes c0 + w, c0 + w + nw,
-    // ...  FP8: each wave writes its own chunk's scales (no barrier and no
-    // LDS round trip, which the decode batch's latency would pay for).
+    // This workgroup's 512-channel chunks c0 .. c1-1: wave w takes c0 + w,
+    // c0 + w + nw, ...  FP8: each wave writes its own chunk's codes and 4
+    // scales (no barrier and no LDS round trip, which the decode batch's
+    // latency would pay for).
     const int nw = nthr >> 6;
     for (int c = cfirst; c < c1; c += nw) {
-        const ChunkData d = finish_chunk<FP8>(c == cfirst ? raw : load_raw<FP8>(x, H, t, c), H,
-                                              c, s_scale);
-        store_chunk<FP8>(d, H, K, c, drow, recv_x);
-        if constexpr (FP8) store_chunk_scales(d, H, K, c, drow, recv_scales);
+        const ChunkData r = c == cfirst ? raw : load_raw<false>(x, H, t, c);
+        if constexpr (FP8)
+            store_half_chunk(quantise_half(r.a), H, K, c, drow, recv_x, recv_scales);
+        else
+            store_chunk<false>(r, H, K, c, drow, recv_x);
     }
 }
 
@@ -772,18 +810,16 @@ hipError_t launch_dispatch(const uint16_t* x, int T, int H, int K, bool fp8, voi
     return hipGetLastError();
 }
 
-size_t ll_dispatch_lds_bytes(int E, int H, bool fp8) {
-    return sizeof(int) * 2 * (size_t)E + (fp8 ? sizeof(float) * (size_t)(H / 128) : 0);
-}
+size_t ll_dispatch_lds_bytes(int E) { return sizeof(int) * 2 * (size_t)E; }
 
 hipError_t launch_ll_dispatch(const uint16_t* x, const int64_t* idx, int T, int H, int K, int E,
                               int C, bool fp8, int32_t* cnt_e, void* recv_x, float* recv_scales,
                               int32_t* recv_src, int32_t* dst_row, int64_t* num_invalid,
                               hipStream_t s) {
-    const int nchunk = (H + dispatch_chunk(fp8) - 1) / dispatch_chunk(fp8);
+    const int nchunk = (H + kLlChunk - 1) / kLlChunk;
     const int nw = kLlWaves;
     static_assert(kLlWaves * 64 <= kDispatchMaxThreads, "block too large");
-    const size_t lds = ll_dispatch_lds_bytes(E, H, fp8);
+    const size_t lds = ll_dispatch_lds_bytes(E);
     if (T == 0) {
         const int64_t rows = (int64_t)E * C > E ? (int64_t)E * C : E;
         hipLaunchKernelGGL(ll_empty_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,

@@ -183,14 +183,17 @@ hipError_t launch_layout_dispatch(const uint16_t* x, const int64_t* idx, int T, 
 // waves past the workgroup's channel chunks only take part in the scan.
 // Eight waves rather than sixteen start sooner and scan sooner (the kernel
 // ended 0.3 us earlier at 128 tokens x 7168, top-8 of 256 experts).  LDS:
-// two [E] int histograms and, for FP8, the token's G scales.
+// two [E] int histograms.  Both dtypes move 512-channel chunks (FP8 too,
+// so that the quantiser of a small batch is spread over more waves).
 constexpr int kLlWaves = 8;
 constexpr int kLlScanUnroll = 4;
+constexpr int kLlChunk = 512;
+static_assert(kLlChunk == kDispatchChunkBf16, "the decode kernel loads and stores bf16 chunks");
 // Workgroups the decode dispatch aims for (one per CU of MI355X): a batch of
 // T < this many tokens splits each token over up to this / T workgroups.
 constexpr int kLlTargetWorkgroups = 256;
 
-size_t ll_dispatch_lds_bytes(int E, int H, bool fp8);
+size_t ll_dispatch_lds_bytes(int E);
 
 hipError_t launch_ll_dispatch(const uint16_t* x, const int64_t* idx, int T, int H, int K, int E,
                               int C, bool fp8, int32_t* cnt_e, void* recv_x, float* recv_scales,
