@@ -274,7 +274,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build models the all-to-all's "
+        print("bench.py measures one GPU only: the library models the all-to-all's "
               "destination partitions as local HBM buffers and has no multi-GPU path; "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)

@@ -60,7 +60,7 @@ extern "C" {
 typedef enum EP_ENUM_BASE {
     EP_OK = 0,
     EP_ERR_INVALID_ARG = 1,  /* null pointer, bad size or inconsistent shape */
-    EP_ERR_UNSUPPORTED = 2,  /* valid but outside this build's limits       */
+    EP_ERR_UNSUPPORTED = 2,  /* valid but outside the library's limits     */
     EP_ERR_WORKSPACE = 3,    /* workspace smaller than ep_workspace_bytes() */
     EP_ERR_HIP = 4           /* a HIP call or kernel launch failed          */
 } ep_status_t;
@@ -70,7 +70,7 @@ typedef enum EP_ENUM_BASE {
     EP_DTYPE_FP8_E4M3 = 1    /* receive rows are OCP E4M3 codes + scales    */
 } ep_dtype_t;
 
-/* Limits of this build (EP_ERR_UNSUPPORTED beyond them). */
+/* Limits of the library (EP_ERR_UNSUPPORTED beyond them). */
 #define EP_MAX_EXPERTS 1024
 #define EP_MAX_TOPK 64
 #define EP_LL_MAX_SLOTS 8192   /* T*K of one ep_low_latency_dispatch call */
