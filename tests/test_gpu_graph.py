@@ -126,3 +126,53 @@ def test_graph_replays_match_eager(name, T, path):
         got = snapshot(*bufs)
         for a, b in zip(got, want):
             np.testing.assert_array_equal(a, b, err_msg="replay %d" % rep)
+
+
+_FIRST_CALL_CAPTURED = r'''
+import sys
+import numpy as np
+import torch
+from combine_ep_get_dispatch_amd import binding as ep
+from combine_ep_get_dispatch_amd import workloads as wl
+
+T, H, K, R = 4096, 7168, 8, 4096 * 8      # tiles of 8 tokens: 112 KiB of LDS per workgroup
+y_bits, dst, w = wl.combine_inputs(T, H, K, R, 311, masked_frac=0.01)
+dev = torch.device("cuda:0")
+y = torch.from_numpy(y_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+d_dst = torch.from_numpy(dst).to(dev)
+d_w = torch.from_numpy(w).to(dev)
+out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+side = torch.cuda.Stream()
+side.wait_stream(torch.cuda.current_stream())
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g, stream=side):      # the process's first combine call
+    ep.combine(y, d_dst, d_w, out=out)
+results = []
+for _ in range(3):
+    out.fill_(0)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    results.append(out.clone())
+eager = ep.combine(y, d_dst, d_w)
+torch.cuda.synchronize()
+ok = all(torch.equal(r.view(torch.int16), eager.view(torch.int16)) for r in results)
+print("first-call capture ok" if ok else "first-call capture MISMATCH", flush=True)
+sys.exit(0 if ok else 1)
+'''
+
+
+def test_first_combine_call_inside_a_capture():
+    """A process whose first combine is made under graph capture, at a shape
+    whose tiles need more than 64 KiB of LDS (so the kernel's LDS cap is
+    raised during the capture): every replay equals an eager call."""
+    import os
+    import subprocess
+    import sys
+    announce("first combine call inside a capture (subprocess)")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _FIRST_CALL_CAPTURED], cwd=root,
+                       capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-2000:])
+    assert "first-call capture ok" in r.stdout
