@@ -110,4 +110,19 @@ __device__ __forceinline__ uint32_t group16_max_u32(uint32_t v) {
     return v;
 }
 
+// Sum over aligned segments of S lanes (S a power of two, 1..64), every lane
+// of a segment receiving its segment's total.  Segments of up to 16 lanes lie
+// inside a DPP row and take DPP moves: neighbour and pair swaps, then the
+// half-row and row mirrors, which pair the halves; wider segments finish with
+// cross-row shuffles.  All 64 lanes must be active.
+__device__ __forceinline__ int segment_sum(int v, int S) {
+    if (S >= 2) v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false);
+    if (S >= 4) v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false);
+    if (S >= 8) v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, false);
+    if (S >= 16) v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, false);
+    if (S >= 32) v += __shfl_xor(v, 16);
+    if (S >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
 }  // namespace ep

@@ -337,9 +337,9 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void dispatch_kernel(
 // and N = sum over j of pre[j][E].  Thread i = k * S + j (S = blocks rounded
 // up to a power of two) loads slot k's packed row and then block j's term
 // for it (k = K: block j's term of N): one round of L2 loads after the row
-// load, spread over (K+1)*S threads.  A shuffle reduction over each S-lane
-// segment gives the row, which reaches the other waves through LDS (one
-// barrier).  The workgroup handling token 0 also writes the counts, offsets
+// load, spread over (K+1)*S threads.  A sum over each S-lane segment
+// (segment_sum: DPP moves inside a 16-lane row) gives the row, which reaches
+// the other waves through LDS (one barrier).  The workgroup handling token 0 also writes the counts, offsets
 // and header.  s_scale ([G]), s_row ([64]) and s_n are the workgroup's LDS.
 template <bool FP8>
 __device__ __forceinline__ void layout_dispatch_token(
@@ -372,7 +372,7 @@ __device__ __forceinline__ void layout_dispatch_token(
         } else if (k == K && j < nb) {
             v = pre[(int64_t)j * (E + 1) + E];
         }
-        for (int o = S >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+        v = segment_sum(v, S);
         if (active && j == 0) {
             if (k < K) {
                 int r = pk >= 0 ? v + (pk & ((1 << kRankBits) - 1)) : -1;
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void layout_dispatch_kernel(
 // data goes to the de-duplicated rows).  Thread i = g * S + j sums block j's
 // terms (and every S-th block's after it) for slot g (g < K: its expert row
 // and its partition row) or for the totals (g = K: N and the number of
-// de-duplicated rows); shuffle reductions over S-lane segments close the
+// de-duplicated rows); sums over S-lane segments (segment_sum) close the
 // sums.  A slot stores the token's data only if it is the first of
 // the token's slots in its partition.  Workgroup 0 writes the counts, offsets
 // and header.
@@ -519,10 +519,8 @@ __global__ __launch_bounds__(kDispatchMaxThreads) void dedup_dispatch_kernel(
                 vp += ppre[(int64_t)j * (P + 1) + P];
             }
         }
-        for (int o = S >> 1; o >= 1; o >>= 1) {
-            ve += __shfl_xor(ve, o);
-            vp += __shfl_xor(vp, o);
-        }
+        ve = segment_sum(ve, S);
+        vp = segment_sum(vp, S);
         if (j0 == 0) {
             if (g < K) {
                 int r = pk >= 0 ? ve + (pk & ((1 << kRankBits) - 1)) : -1;
