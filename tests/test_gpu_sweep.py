@@ -7,8 +7,10 @@ path, the one-call path under a random CU budget, the de-duplicated path, the al
 with a random alignment and (when T*K allows) the fixed-capacity decode
 path, and compared with the
 oracle to the usual bars (bit-exact layout, rows and scales; combine within
-2 bf16 ulp).  The draws are fixed by the seed, so a failure names a
-reproducible case.
+2 bf16 ulp).  Six more draws are top-8 batches of 1024 to 5000 tokens with
+ragged widths, where combine runs in tiles of consecutive tokens, through
+the two-call, one-call and de-duplicated paths.  The draws are fixed by the
+seed, so a failure names a reproducible case.
 """
 import numpy as np
 import pytest
@@ -57,3 +59,35 @@ def test_sweep(T, H, E, P, K, seed, kw, budget, align):
     if T * K <= 8192:
         check_ll(case.topk_idx, case.x_bits, case.topk_weights, E, max(1, T // 3), case.fp8,
                  label, y_seed=seed + 1)
+
+
+def _draw_top8(i):
+    rng = np.random.default_rng(9500 + i)
+    E = int(rng.choice([8, 32, 64, 256]))
+    divisors = [d for d in range(1, E + 1) if E % d == 0]
+    P = int(rng.choice(divisors))
+    T = int(rng.integers(1024, 5000))
+    fp8 = bool(rng.integers(0, 2))
+    H = int(rng.choice([640, 1152, 3200, 7168])) if fp8 else \
+        int(rng.choice([136, 520, 1032, 4104]))
+    kw = dict(masked_frac=float(rng.choice([0.0, 0.05, 0.3])),
+              invalid_frac=float(rng.choice([0.0, 0.02])),
+              allow_dup=bool(rng.integers(0, 2)), skew=float(rng.choice([0.0, 1.0, 3.0])),
+              fp8=fp8)
+    return T, H, E, P, 8, 9600 + i, kw
+
+
+SWEEP_TOP8 = [_draw_top8(i) for i in range(6)]
+
+
+@pytest.mark.parametrize("T,H,E,P,K,seed,kw", SWEEP_TOP8,
+                         ids=["t%d_T%d_H%d_E%d_P%d" % ((i,) + c[:4]) for i, c in enumerate(SWEEP_TOP8)])
+def test_sweep_top8_batches(T, H, E, P, K, seed, kw):
+    """Top-8 batches of 1024 tokens or more, where combine runs in tiles of
+    consecutive tokens (ragged tails, ragged widths): the two-call, one-call
+    and de-duplicated paths against the oracle."""
+    case = wl.random_case(T, H, E, P, K, seed, **kw)
+    label = "top-8 sweep seed=%d" % seed
+    check_case(case, label=label)
+    check_case(case, label=label, one_call=True)
+    check_dedup(case, label)
